@@ -1,0 +1,275 @@
+"""block_sparse_attention_amd — block-sparse FlashAttention forward for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbsattn.so`` (``include/bsattn.h``).
+Functions carry the C names; they take torch tensors that live on the GPU,
+pass their device pointers and the current HIP stream, and return the output
+tensors.  Torch is used for device memory and streams only: every step of
+the computation runs in the library's HIP kernels.  There is no fallback —
+if the library is not built, or a tensor is not on the GPU, the call raises.
+
+Build the library with ``python -m block_sparse_attention_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "BLOCK", "BsattnError", "load_library", "bsattn_status_string", "bsattn_version",
+    "bsattn_build_mask_topk", "bsattn_build_mask_threshold", "bsattn_mask_to_indices",
+    "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices",
+    "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
+    "bsattn_decode_gqa", "EXPORTED_SYMBOLS",
+]
+
+BLOCK = 64
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
+
+EXPORTED_SYMBOLS = (
+    "bsattn_status_string", "bsattn_version", "bsattn_build_mask_topk",
+    "bsattn_build_mask_threshold", "bsattn_mask_to_indices", "bsattn_fwd_workspace_bytes",
+    "bsattn_fwd", "bsattn_fwd_indices", "bsattn_decode_num_splits",
+    "bsattn_decode_workspace_bytes", "bsattn_decode_gqa", "bsattn_decode_default_splits",
+)
+
+_STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
+           3: "BSATTN_ERR_UNSUPPORTED", 4: "BSATTN_ERR_WORKSPACE", 5: "BSATTN_ERR_HIP"}
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "bsattn_status_string": (ctypes.c_char_p, [_I]),
+    "bsattn_version": (ctypes.c_char_p, []),
+    "bsattn_build_mask_topk": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_build_mask_threshold": (_I, [_P, _I, _I, _I, _F, _I, _I, _P, _P]),
+    "bsattn_mask_to_indices": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "bsattn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "bsattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_fwd_indices": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
+    "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "bsattn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbsattn.so (once) and declare the C signatures.  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m block_sparse_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def bsattn_status_string(status: int) -> str:
+    return load_library().bsattn_status_string(status).decode()
+
+
+def bsattn_version() -> str:
+    return load_library().bsattn_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise BsattnError(fn, status, bsattn_status_string(status))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name: str, dtype, ndim: Optional[int] = None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+    return t
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+def bsattn_build_mask_topk(scores, topk: int, dense_last_two_rows: bool = False,
+                           force_diagonal: bool = True, out=None, stream=None):
+    """scores float32 [B,H,nb,nb] -> uint8 0/1 mask (TileLang block-sparse guide §3.1)."""
+    torch = _torch()
+    _dev(scores, "scores", torch.float32, 4)
+    B, H, nb, nb2 = scores.shape
+    if nb != nb2:
+        raise ValueError("scores must be [B, H, nb, nb]")
+    if out is None:
+        out = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=scores.device)
+    _dev(out, "out", torch.uint8, 4)
+    _check("bsattn_build_mask_topk", load_library().bsattn_build_mask_topk(
+        _ptr(scores), B, H, nb, int(topk), int(bool(dense_last_two_rows)),
+        int(bool(force_diagonal)), _ptr(out), _stream(stream)))
+    return out
+
+
+def bsattn_build_mask_threshold(scores, threshold: float, dense_last_two_rows: bool = False,
+                                force_diagonal: bool = True, out=None, stream=None):
+    """scores float32 [B,H,nb,nb] -> uint8 0/1 mask, score > threshold (guide §3.2)."""
+    torch = _torch()
+    _dev(scores, "scores", torch.float32, 4)
+    B, H, nb, nb2 = scores.shape
+    if nb != nb2:
+        raise ValueError("scores must be [B, H, nb, nb]")
+    if out is None:
+        out = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=scores.device)
+    _dev(out, "out", torch.uint8, 4)
+    _check("bsattn_build_mask_threshold", load_library().bsattn_build_mask_threshold(
+        _ptr(scores), B, H, nb, float(threshold), int(bool(dense_last_two_rows)),
+        int(bool(force_diagonal)), _ptr(out), _stream(stream)))
+    return out
+
+
+def bsattn_mask_to_indices(mask, is_causal: bool = True, stream=None) -> Tuple[object, object]:
+    """uint8 mask [B,H,nb,nb] -> (idx int32 [B,H,nb,nb] ascending, -1 padded; cnt int32 [B,H,nb])."""
+    torch = _torch()
+    _dev(mask, "mask", torch.uint8, 4)
+    B, H, nb, _ = mask.shape
+    idx = torch.empty((B, H, nb, nb), dtype=torch.int32, device=mask.device)
+    cnt = torch.empty((B, H, nb), dtype=torch.int32, device=mask.device)
+    _check("bsattn_mask_to_indices", load_library().bsattn_mask_to_indices(
+        _ptr(mask), B, H, nb, int(bool(is_causal)), _ptr(idx), _ptr(cnt), _stream(stream)))
+    return idx, cnt
+
+
+def bsattn_fwd_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
+    return int(load_library().bsattn_fwd_workspace_bytes(B, H, S, D))
+
+
+def _qkv(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, torch.bfloat16, 4)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    return q.shape
+
+
+def bsattn_fwd(q, k, v, block_mask, is_causal: bool = True, out=None, workspace=None, stream=None):
+    """Block-sparse attention forward (guide §4).  q,k,v bf16 [B,H,S,D]; mask uint8 [B,H,nb,nb]."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    _dev(block_mask, "block_mask", torch.uint8, 4)
+    nb = -(-S // BLOCK)
+    if tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError(f"block_mask must be [{B}, {H}, {nb}, {nb}]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, 4)
+    need = bsattn_fwd_workspace_bytes(B, H, S, D)
+    ws_ptr, ws_bytes = 0, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("bsattn_fwd", load_library().bsattn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), B, H, S, D, int(bool(is_causal)),
+        _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stream=None):
+    """Forward pass from precomputed lists (output of bsattn_mask_to_indices)."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    nb = -(-S // BLOCK)
+    _dev(idx, "idx", torch.int32, 4)
+    _dev(cnt, "cnt", torch.int32, 3)
+    if tuple(idx.shape) != (B, H, nb, nb) or tuple(cnt.shape) != (B, H, nb):
+        raise ValueError("idx must be [B,H,nb,nb] and cnt [B,H,nb]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, 4)
+    _check("bsattn_fwd_indices", load_library().bsattn_fwd_indices(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), B, H, S, D, int(bool(is_causal)),
+        _ptr(out), _stream(stream)))
+    return out
+
+
+def bsattn_decode_num_splits(B: int, Hq: int, Hkv: int, max_selected_blocks: int, D: int,
+                             num_cus: int) -> int:
+    return int(load_library().bsattn_decode_num_splits(B, Hq, Hkv, max_selected_blocks, D, num_cus))
+
+
+def bsattn_decode_default_splits(B: int, Hq: int, Hkv: int, max_selected_blocks: int, D: int) -> int:
+    return int(load_library().bsattn_decode_default_splits(B, Hq, Hkv, max_selected_blocks, D))
+
+
+def bsattn_decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> int:
+    return int(load_library().bsattn_decode_workspace_bytes(B, Hq, D, num_splits))
+
+
+def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0, out=None,
+                      workspace=None, stream=None):
+    """Split-KV sparse GQA decode (guide §6).  q bf16 [B,Hq,D]; k,v bf16 [total_k,Hkv,D];
+    cu_seqlens_k int32 [B+1]; block_indices int32 [B,Hkv,max_sel] (-1 = empty)."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k, "k", torch.bfloat16, 3)
+    _dev(v, "v", torch.bfloat16, 3)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    _dev(block_indices, "block_indices", torch.int32, 3)
+    B, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError("k and v must be [total_k, Hkv, D] with the query's D")
+    if cu_seqlens_k.numel() != B + 1 or block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
+        raise ValueError("cu_seqlens_k must be [B+1] and block_indices [B, Hkv, max_sel]")
+    max_sel = block_indices.shape[2]
+    ns = int(num_splits)
+    if ns <= 0:
+        ns = bsattn_decode_default_splits(B, Hq, Hkv, max_sel, D)
+        if ns <= 0:
+            raise BsattnError("bsattn_decode_default_splits", 5, "could not query the device")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", torch.bfloat16, 3)
+    need = bsattn_decode_workspace_bytes(B, Hq, D, ns)
+    ws_ptr, ws_bytes = 0, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("bsattn_decode_gqa", load_library().bsattn_decode_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
+        max_sel, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out

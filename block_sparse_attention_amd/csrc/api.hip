@@ -1,0 +1,228 @@
+// C ABI of the block-sparse attention library: argument checks and launches.
+// All checks run before anything is enqueued; see include/bsattn.h.
+#include <atomic>
+#include <math.h>
+
+#include "../../include/bsattn.h"
+#include "launch.hpp"
+
+using namespace bsattn;
+
+namespace {
+
+inline hipStream_t as_hip(bsattn_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool head_dim_ok(int D) { return D == 64 || D == 128; }
+
+inline int nblocks(int n) { return (n + BSATTN_BLOCK - 1) / BSATTN_BLOCK; }
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// int32 sizes whose products index 64-bit element offsets
+inline bool fits_elems(long double n) { return n < 9.0e18L; }
+
+// Split count of the guide's heuristic (TileLang block-sparse Flash-Attention
+// guide, §6.3), written for decode: one (batch, KV head) pair is one m-block.
+int heuristic_splits(int B, int Hq, int Hkv, int max_sel, int D, int num_cus) {
+  const int group = Hq / Hkv;
+  const int valid_block_h = group < 64 ? group : 64;
+  const long long total_mblocks = (long long)B * (Hq / valid_block_h);
+  const long long num_n_blocks = max_sel;
+  const long long num_m_blocks = 1;
+  const double size_one_kv_head = (double)max_sel * BSATTN_BLOCK * (D + D) * 2.0;
+  const double l2 = 50.0 * 1024 * 1024;
+  const bool causal_or_local = true;
+  const int max_splits = 128;
+  if (total_mblocks >= 0.8 * num_cus) {
+    if (size_one_kv_head > l2 && num_m_blocks >= 2LL * num_cus && !causal_or_local) {
+      long long s = (long long)ceil(size_one_kv_head / l2);
+      return (int)(s < max_splits ? s : max_splits);
+    }
+    return 1;
+  }
+  if (num_n_blocks <= 4) return 1;
+  long long cap = max_splits;
+  if (num_cus < cap) cap = num_cus;
+  if (num_n_blocks < cap) cap = num_n_blocks;
+  double best = 0.0;
+  for (long long s = 1; s <= cap; ++s) {
+    const double waves = (double)total_mblocks * s / num_cus;
+    const double eff = waves / ceil(waves);
+    if (eff > best) best = eff;
+  }
+  for (long long s = 1; s <= cap; ++s) {
+    const double waves = (double)total_mblocks * s / num_cus;
+    const double eff = waves / ceil(waves);
+    if (eff >= 0.85 * best) return (int)s;
+  }
+  return 1;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64 && cus > 0) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+size_t decode_ws(int B, int Hq, int D, int ns) {
+  if (ns <= 1) return 0;
+  const size_t parts = (size_t)B * Hq * ns;
+  return align_up(parts * D * sizeof(float)) + align_up(parts * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsattn_status_string(bsattn_status s) {
+  switch (s) {
+    case BSATTN_OK: return "ok";
+    case BSATTN_ERR_NULL: return "null pointer argument";
+    case BSATTN_ERR_SHAPE: return "size out of range or inconsistent";
+    case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; decode group size <= 16)";
+    case BSATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case BSATTN_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+const char* bsattn_version(void) { return "0.1.0"; }
+
+bsattn_status bsattn_build_mask_topk(const float* scores, int B, int H, int nb, int topk,
+                                     int dense_last_two_rows, int force_diagonal, uint8_t* mask,
+                                     bsattn_stream_t stream) {
+  if (!scores || !mask) return BSATTN_ERR_NULL;
+  if (B <= 0 || H <= 0 || nb <= 0 || topk < 0 || topk > nb) return BSATTN_ERR_SHAPE;
+  if ((long long)B * H * nb > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  return launch_mask_topk(scores, B, H, nb, topk, dense_last_two_rows ? 1 : 0,
+                          force_diagonal ? 1 : 0, mask, as_hip(stream)) == hipSuccess
+             ? BSATTN_OK
+             : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_build_mask_threshold(const float* scores, int B, int H, int nb,
+                                          float threshold, int dense_last_two_rows,
+                                          int force_diagonal, uint8_t* mask,
+                                          bsattn_stream_t stream) {
+  if (!scores || !mask) return BSATTN_ERR_NULL;
+  if (B <= 0 || H <= 0 || nb <= 0) return BSATTN_ERR_SHAPE;
+  return launch_mask_threshold(scores, B, H, nb, threshold, dense_last_two_rows ? 1 : 0,
+                               force_diagonal ? 1 : 0, mask, as_hip(stream)) == hipSuccess
+             ? BSATTN_OK
+             : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, int is_causal,
+                                     int32_t* idx, int32_t* cnt, bsattn_stream_t stream) {
+  if (!mask || !idx || !cnt) return BSATTN_ERR_NULL;
+  if (B <= 0 || H <= 0 || nb <= 0) return BSATTN_ERR_SHAPE;
+  if ((long long)B * H * nb / 4 + 1 > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  return launch_compact(mask, B, H, nb, is_causal ? 1 : 0, idx, cnt, as_hip(stream)) == hipSuccess
+             ? BSATTN_OK
+             : BSATTN_ERR_HIP;
+}
+
+size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
+  (void)B; (void)H; (void)S; (void)D;
+  return 0;
+}
+
+static bsattn_status fwd_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint8_t* mask, const int32_t* idx, const int32_t* cnt,
+                                int B, int H, int S, int D, int is_causal, uint16_t* out,
+                                hipStream_t stream) {
+  if (B <= 0 || H <= 0 || S <= 0) return BSATTN_ERR_SHAPE;
+  if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H * nblocks(S) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (!fits_elems((long double)B * H * S * D)) return BSATTN_ERR_SHAPE;
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.mask = mask; a.idx = idx; a.cnt = cnt;
+  a.B = B; a.H = H; a.S = S; a.D = D; a.nb = nblocks(S);
+  a.causal = is_causal ? 1 : 0;
+  return launch_prefill(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint8_t* block_mask, int B, int H, int S, int D, int is_causal,
+                         uint16_t* out, void* workspace, size_t workspace_bytes,
+                         bsattn_stream_t stream) {
+  if (!q || !k || !v || !block_mask || !out) return BSATTN_ERR_NULL;
+  if (B > 0 && H > 0 && S > 0 && head_dim_ok(D)) {
+    const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
+  }
+  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, S, D, is_causal, out,
+                    as_hip(stream));
+}
+
+bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* idx, const int32_t* cnt, int B, int H, int S,
+                                 int D, int is_causal, uint16_t* out, bsattn_stream_t stream) {
+  if (!q || !k || !v || !idx || !cnt || !out) return BSATTN_ERR_NULL;
+  return fwd_common(q, k, v, nullptr, idx, cnt, B, H, S, D, is_causal, out, as_hip(stream));
+}
+
+int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,
+                             int num_cus) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_selected_blocks <= 0 || D <= 0 ||
+      num_cus <= 0)
+    return 0;
+  return heuristic_splits(B, Hq, Hkv, max_selected_blocks, D, num_cus);
+}
+
+int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return 0;
+  int s = bsattn_decode_num_splits(B, Hq, Hkv, max_selected_blocks, D, cus);
+  if (s > max_selected_blocks) s = max_selected_blocks;
+  return s;
+}
+
+size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  return decode_ws(B, Hq, D, num_splits);
+}
+
+bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* cu_seqlens_k, const int32_t* block_indices, int B,
+                                int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
+                                int num_splits, uint16_t* out, void* workspace,
+                                size_t workspace_bytes, bsattn_stream_t stream) {
+  if (!q || !k || !v || !cu_seqlens_k || !block_indices || !out) return BSATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_selected_blocks <= 0 || total_k <= 0)
+    return BSATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return BSATTN_ERR_SHAPE;
+  if (num_splits > max_selected_blocks) return BSATTN_ERR_SHAPE;
+  if (!head_dim_ok(D) || Hq / Hkv > 16) return BSATTN_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535) return BSATTN_ERR_SHAPE;
+  int ns = num_splits;
+  if (ns <= 0) {
+    ns = bsattn_decode_default_splits(B, Hq, Hkv, max_selected_blocks, D);
+    if (ns <= 0) return BSATTN_ERR_HIP;
+  }
+  const size_t need = decode_ws(B, Hq, D, ns);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices; a.out = out;
+  const size_t parts = (size_t)B * Hq * ns;
+  a.o_part = (float*)workspace;
+  a.lse = need ? (float*)((char*)workspace + align_up(parts * D * sizeof(float))) : nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.max_sel = max_selected_blocks;
+  a.total_k = total_k; a.num_splits = ns;
+  return launch_decode(a, as_hip(stream)) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+}  // extern "C"

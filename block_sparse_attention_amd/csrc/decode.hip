@@ -1,0 +1,303 @@
+// Split-KV sparse GQA decode for gfx950 (one query token per sequence).
+//
+// What is computed follows the TileLang block-sparse Flash-Attention guide,
+// §6–§6.2: for each (batch, KV head) the list of selected 64-token blocks is
+// cut into num_splits contiguous ranges (the first slots % splits ranges one
+// slot longer); padded (-1) and out-of-range entries are skipped; keys at or
+// beyond the sequence length are masked; each range produces a normalised
+// partial output and its base-2 log-sum-exp, and a merge kernel combines the
+// ranges with weights 2^(lse - max lse) (§6.1).  Query head hq reads KV head
+// hq / (Hq / Hkv).
+//
+// CDNA4 mapping (not the guide's kernel design):
+// * one work-group of 4 wave64s per (batch, KV head, split); the waves take
+//   the range's slots round-robin and are combined through LDS at the end;
+// * per 64-token block, S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
+//   group's query heads as the 16 columns (K rows loaded straight from HBM
+//   into the A-operand layout, 16 bytes per lane);
+// * the exponentiated scores are already the B operand of O^T = V^T . P^T;
+//   V goes through LDS, read transposed with ds_read_b64_tr_b16;
+// * all K and V loads of a block are issued before any of its math, so each
+//   wave keeps 2 * 64 * D * 2 bytes in flight.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bsattn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D>
+struct DCfg {
+  static constexpr int kStride = D + 16;     // LDS row stride of a V half tile
+  static constexpr int kSteps = D / 32;      // k-steps of S^T = K . Q^T
+  static constexpr int kDT = D / 16;         // 16-row tiles of O^T
+  static constexpr int kRowChunks = D / 8;   // 16-byte chunks per token row
+  static constexpr int kVPer = 64 * kRowChunks / kWave;  // V chunks per lane per block
+  static constexpr int kWaveLds = 32 * kStride;          // bf16 elements per wave
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int final_out) {
+  using C = DCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * C::kWaveLds];
+
+  const int sid = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int ns = a.num_splits;
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;     // query column of the 16x16 tiles
+  const int grp = lane >> 4;     // k-group / row group
+  uint16_t* Vs = lds + w * C::kWaveLds;
+
+  // sequence extent; a malformed range is treated as empty
+  const int start = a.cu_seqlens[b];
+  const int end = a.cu_seqlens[b + 1];
+  const int len = (end >= start && end <= a.total_k && start >= 0) ? end - start : 0;
+  const int nbb = (len + 63) / 64;
+
+  // this split's slot range
+  const int nslots = a.max_sel;
+  const int bps = nslots / ns;
+  const int rem = nslots % ns;
+  const int my_len = bps + (sid < rem ? 1 : 0);
+  const int my_start = bps * sid + min(sid, rem);
+
+  const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive tokens
+  const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+
+  // Q^T as the B operand: column col = query head kvh*G + col (zero when col >= G).
+  u32x4 qf[C::kSteps];
+  {
+    const int hq = kvh * G + col;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      if (col < G)
+        qf[s] = *(const u32x4*)(a.q + ((int64_t)b * a.Hq + hq) * D + 32 * s + 8 * grp);
+      else
+        qf[s] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  f32x4 o[C::kDT];
+#pragma unroll
+  for (int t = 0; t < C::kDT; ++t) o[t] = f32x4{};
+  float m = -INFINITY;
+  float l = 0.0f;
+
+  const int32_t* idx_row = a.block_indices + ((int64_t)b * a.Hkv + kvh) * nslots;
+  const int tr_r = (lane >> 2) & 3;
+  const int tr_m = lane & 3;
+
+  for (int slot = my_start + w; slot < my_start + my_len; slot += kWaves) {
+    const int blk = __builtin_amdgcn_readfirstlane(idx_row[slot]);
+    if (blk < 0 || blk >= nbb) continue;
+    const int tok0 = blk * 64;
+    const int ntok = min(64, len - tok0);
+    const uint16_t* __restrict__ Kp = a.k + ((int64_t)start + tok0) * row_stride + (int64_t)kvh * D;
+    const uint16_t* __restrict__ Vp = a.v + ((int64_t)start + tok0) * row_stride + (int64_t)kvh * D;
+
+    // issue every load of the block first
+    u32x4 kf[4][C::kSteps];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + col;
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        if (tok < ntok)
+          kf[tt][s] = *(const u32x4*)(Kp + tok * row_stride + 32 * s + 8 * grp);
+        else
+          kf[tt][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+    u32x4 vr[C::kVPer];
+#pragma unroll
+    for (int t = 0; t < C::kVPer; ++t) {
+      const int chunk = lane + kWave * t;
+      const int tok = chunk / C::kRowChunks;
+      const int c8 = chunk % C::kRowChunks;
+      if (tok < ntok)
+        vr[t] = *(const u32x4*)(Vp + tok * row_stride + c8 * 8);
+      else
+        vr[t] = u32x4{0, 0, 0, 0};
+    }
+
+    // S^T tiles: token 16*tt + 4*grp + r, query column col
+    f32x4 sc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      sc[tt] = f32x4{};
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) sc[tt] = mfma16(kf[tt][s], qf[s], sc[tt]);
+    }
+    if (ntok < 64) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * tt + 4 * grp + r >= ntok) sc[tt][r] = -INFINITY;
+    }
+
+    float mx = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[tt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = fast_exp2((m - m_use) * c);
+    const float mc = m_use * c;
+    float rs = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[tt][r] = fast_exp2(fmaf(sc[tt][r], c, -mc));
+        rs += sc[tt][r];
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] *= alpha;
+
+    // O^T += V^T . P^T in two 32-token halves, each staged through LDS
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      wave_lds_sync();  // previous reads of this wave's buffer are done
+#pragma unroll
+      for (int t = 0; t < C::kVPer / 2; ++t) {
+        const int chunk = lane + kWave * (t + u * (C::kVPer / 2));
+        const int tok = chunk / C::kRowChunks - 32 * u;
+        const int c8 = chunk % C::kRowChunks;
+        *(u32x4*)(Vs + tok * C::kStride + c8 * 8) = vr[t + u * (C::kVPer / 2)];
+      }
+      wave_lds_sync();
+      const u32x4 pb = u32x4{pack_bf16x2(sc[2 * u][0], sc[2 * u][1]),
+                             pack_bf16x2(sc[2 * u][2], sc[2 * u][3]),
+                             pack_bf16x2(sc[2 * u + 1][0], sc[2 * u + 1][1]),
+                             pack_bf16x2(sc[2 * u + 1][2], sc[2 * u + 1][3])};
+      const int row0 = 4 * grp + tr_r;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t) {
+        const int cc = 16 * t + 4 * tr_m;
+        const u32x2 lo = lds_read_tr16(Vs + row0 * C::kStride + cc);
+        const u32x2 hi = lds_read_tr16(Vs + (row0 + 16) * C::kStride + cc);
+        o[t] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[t]);
+      }
+    }
+  }
+
+  // ---- combine the four waves of this split ----
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  wave_lds_sync();
+  __syncthreads();
+  float* red = (float*)(lds + w * C::kWaveLds);   // [16 m][16 l][16 * D o]
+  if (grp == 0) {
+    red[col] = m;
+    red[16 + col] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[32 + col * D + 16 * t + 4 * grp + r] = o[t][r];
+  __syncthreads();
+
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int qn = e / D;
+    const int d = e - qn * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ((float*)(lds + ww * C::kWaveLds))[qn]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float* rw = (const float*)(lds + ww * C::kWaveLds);
+        const float mw = rw[qn];
+        const float wt = (mw == -INFINITY) ? 0.0f : fast_exp2((mw - M) * c);
+        L += rw[16 + qn] * wt;
+        acc += rw[32 + qn * D + d] * wt;
+      }
+    }
+    const float val = L > 0.0f ? acc / L : 0.0f;
+    const int hq = kvh * G + qn;
+    if (final_out) {
+      a.out[((int64_t)b * a.Hq + hq) * D + d] = float_to_bf16_bits(val);
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + hq) * ns + sid;
+      a.o_part[pi * D + d] = val;
+      if (d == 0) a.lse[pi] = L > 0.0f ? M * c + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
+// One work-group per (batch, query head): weights 2^(lse_s - max lse).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int64_t bq = blockIdx.x;
+  const int ns = a.num_splits;
+  const int d = threadIdx.x;
+  const float* lse = a.lse + bq * ns;
+  const float* op = a.o_part + bq * ns * D;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[s]);
+  float num = 0.0f, den = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < ns; ++s) {
+      const float ls = lse[s];
+      const float wt = (ls == -INFINITY) ? 0.0f : fast_exp2(ls - M);
+      den += wt;
+      num += wt * op[(int64_t)s * D + d];
+    }
+  }
+  a.out[bq * D + d] = float_to_bf16_bits(den > 0.0f ? num / den : 0.0f);
+}
+
+template <int D>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const int final_out = a.num_splits == 1 ? 1 : 0;
+  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(a.num_splits, a.Hkv, a.B), dim3(kThreads), 0,
+                     stream, a, final_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || final_out) return e;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(D), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.D == 64 ? launch_t<64>(a, stream) : launch_t<128>(a, stream);
+}
+
+}  // namespace bsattn

@@ -1,0 +1,43 @@
+// Internal launchers: host functions that enqueue the kernels.  Arguments are
+// validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+hipError_t launch_mask_topk(const float* scores, int B, int H, int nb, int topk, int dense2,
+                            int diag, uint8_t* mask, hipStream_t stream);
+hipError_t launch_mask_threshold(const float* scores, int B, int H, int nb, float thr,
+                                 int dense2, int diag, uint8_t* mask, hipStream_t stream);
+hipError_t launch_compact(const uint8_t* mask, int B, int H, int nb, int causal, int32_t* idx,
+                          int32_t* cnt, hipStream_t stream);
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  const uint8_t* mask;   // [B,H,nb,nb] mask form, or nullptr
+  const int32_t* idx;    // [B,H,nb,nb] list form, or nullptr
+  const int32_t* cnt;    // [B,H,nb]
+  int B, H, S, D, nb;
+  int causal;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cu_seqlens;
+  const int32_t* block_indices;
+  uint16_t* out;
+  float* o_part;   // [B, Hq, ns, D]
+  float* lse;      // [B, Hq, ns]
+  int B, Hq, Hkv, D, max_sel, total_k, num_splits;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace bsattn

@@ -124,8 +124,8 @@ CONFIGS: Dict[str, object] = {
 }
 
 
-def prefill_inputs(cfg: PrefillConfig, seed: int = 0) -> Dict[str, np.ndarray]:
-    """Scores (float32 [B,H,nb,nb]) and q/k/v (bf16 bits [B,H,S,D])."""
+def prefill_scores(cfg: PrefillConfig, seed: int = 0) -> np.ndarray:
+    """Block importance scores, float32 [B, H, nb, nb]."""
     nb = cfg.nb
     shp = (cfg.B, cfg.H, nb, nb)
     g = child_rng(seed, TAG_SCORES)
@@ -137,13 +137,25 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = 0) -> Dict[str, np.ndarray]:
         raise ValueError(cfg.scores_dist)
     if cfg.force_first_column:
         scores[..., 0] = np.float32(100.0)
-    out = {"scores": scores}
+    return scores
+
+
+def prefill_qkv(cfg: PrefillConfig, seed: int = 0) -> Dict[str, np.ndarray]:
+    """q, k, v as bfloat16 bits [B, H, S, D]."""
+    out = {}
     qkv_shape = (cfg.B, cfg.H, cfg.S, cfg.D)
     for name, tag in (("q", TAG_Q), ("k", TAG_K), ("v", TAG_V)):
         x = child_rng(seed, tag).standard_normal(qkv_shape, dtype=np.float32)
         if cfg.qkv_scale != 1.0:
             x *= np.float32(cfg.qkv_scale)
         out[name] = f32_to_bf16_bits(x)
+    return out
+
+
+def prefill_inputs(cfg: PrefillConfig, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Scores (float32 [B,H,nb,nb]) and q/k/v (bf16 bits [B,H,S,D])."""
+    out = {"scores": prefill_scores(cfg, seed)}
+    out.update(prefill_qkv(cfg, seed))
     return out
 
 

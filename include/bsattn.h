@@ -1,0 +1,194 @@
+/*
+ * bsattn.h — block-sparse FlashAttention forward for AMD MI355X (gfx950).
+ *
+ * Plain C ABI.  Every tensor argument is a caller-owned, contiguous, row-major
+ * DEVICE buffer; bfloat16 tensors are passed as their uint16 bit patterns.
+ * The library never allocates device memory, keeps no mutable global state
+ * and never synchronises the host: each call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the default stream).  Outputs are valid
+ * once the stream reaches the end of the call.  Equal inputs give bitwise
+ * equal outputs (no atomics on any value path).
+ *
+ * Errors: all argument checks run on the host BEFORE any launch.  On an
+ * error nothing is enqueued and no output is touched.  A launch failure
+ * reported by the HIP runtime returns BSATTN_ERR_HIP.  Data content is never
+ * an error: a nonzero mask byte means "selected", a block index outside the
+ * valid range selects nothing; non-finite scores give unspecified masks.
+ *
+ * The block size is fixed at 64 tokens (BSATTN_BLOCK) for both the query and
+ * the key/value dimension, as in the TileLang block-sparse Flash-Attention
+ * guide (§4.1: block_M = block_N = 64, equal to the mask's downsampling
+ * block).
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSATTN_BLOCK 64
+
+typedef struct ihipStream_t* bsattn_stream_t; /* same type as hipStream_t */
+
+typedef enum bsattn_status {
+  BSATTN_OK = 0,
+  BSATTN_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  BSATTN_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree          */
+  BSATTN_ERR_UNSUPPORTED = 3, /* valid but not built (head dim, group size)        */
+  BSATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  BSATTN_ERR_HIP = 5          /* the HIP runtime reported an error at launch time  */
+} bsattn_status;
+
+/* Static text for a status code (never NULL). */
+const char* bsattn_status_string(bsattn_status s);
+
+/* Library version as "major.minor.patch". */
+const char* bsattn_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Block masks                                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Top-k block mask (TileLang block-sparse Flash-Attention guide, §3.1).
+ *   scores : float32 [B, H, nb, nb], block importance scores; row i holds the
+ *            scores of key blocks 0..nb-1 for query block i.
+ *   mask   : uint8   [B, H, nb, nb], written with 0/1.
+ * Per row, the `topk` highest scores over the WHOLE row are selected (ties go
+ * to the lower column index).  Then, if dense_last_two_rows, rows nb-2 and
+ * nb-1 are set all ones (before the causal cut, as in the guide's builder);
+ * then every column j > i is cleared (tril); then, if force_diagonal, the
+ * diagonal block is set (the causal diagonal block is always kept in the
+ * XAttention guide, "algorithm flow", phase 3).
+ * Errors: NULL pointers; B, H, nb <= 0 or topk < 0 or topk > nb (SHAPE).
+ */
+bsattn_status bsattn_build_mask_topk(const float* scores, int B, int H, int nb, int topk,
+                                     int dense_last_two_rows, int force_diagonal, uint8_t* mask,
+                                     bsattn_stream_t stream);
+
+/*
+ * Threshold block mask (same guide, §3.2): a block is selected when its score
+ * is strictly greater than `threshold`; then the same dense-last-two-rows,
+ * tril and diagonal steps as bsattn_build_mask_topk.
+ * Errors: NULL pointers; B, H, nb <= 0 (SHAPE).
+ */
+bsattn_status bsattn_build_mask_threshold(const float* scores, int B, int H, int nb,
+                                          float threshold, int dense_last_two_rows,
+                                          int force_diagonal, uint8_t* mask,
+                                          bsattn_stream_t stream);
+
+/*
+ * Compaction of a block mask into per-row active-block lists: the list form
+ * of the causal loop bound and the block-skip branch of the same guide, §4.4.
+ *   mask : uint8 [B, H, nb, nb], nonzero = selected.
+ *   idx  : int32 [B, H, nb, nb]; row (b,h,i) lists ascending every j with
+ *          mask != 0 (and j <= i when is_causal), then -1 padding.
+ *   cnt  : int32 [B, H, nb], the list lengths.
+ * Errors: NULL pointers; B, H, nb <= 0 (SHAPE).
+ */
+bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, int is_causal,
+                                     int32_t* idx, int32_t* cnt, bsattn_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Block-sparse attention forward (same guide, §4: the block-sparse
+ * Flash-Attention kernel; §5: its reference check).
+ *   q, k, v, out : bfloat16 [B, H, S, D] (K/V heads = query heads).
+ *   block_mask   : uint8 [B, H, nb, nb] with nb = ceil(S / 64); nonzero =
+ *                  query block i attends to key block j.
+ * For query row r the visible keys are the tokens t < S of the selected key
+ * blocks, with t <= r when is_causal; out[r] = softmax(q_r . k_t / sqrt(D)) V
+ * over those keys (fp32 accumulation, probabilities rounded to bfloat16
+ * before the P.V product, output rounded to nearest even).  A row that sees
+ * no key is written as zeros.  Each query block's mask row is compacted on
+ * the device into its ascending active-block list before the block loop.
+ * workspace may be NULL when bsattn_fwd_workspace_bytes returns 0.
+ * Errors: NULL pointers; B, H, S <= 0 (SHAPE); D not 64 or 128 (UNSUPPORTED);
+ * workspace_bytes below bsattn_fwd_workspace_bytes (WORKSPACE).
+ */
+size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D);
+
+bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint8_t* block_mask, int B, int H, int S, int D, int is_causal,
+                         uint16_t* out, void* workspace, size_t workspace_bytes,
+                         bsattn_stream_t stream);
+
+/*
+ * The same forward pass driven by precomputed lists (the output of
+ * bsattn_mask_to_indices with the same is_causal): idx int32 [B, H, nb, nb]
+ * and cnt int32 [B, H, nb].  List entries outside [0, nb) are skipped, and
+ * with is_causal entries above the diagonal are skipped.  For callers that
+ * reuse one mask across many calls.  Errors as bsattn_fwd.
+ */
+bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* idx, const int32_t* cnt, int B, int H, int S,
+                                 int D, int is_causal, uint16_t* out, bsattn_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse GQA decode                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Split count for bsattn_decode_gqa (same guide, §6.3: the smallest split
+ * count whose wave efficiency n_waves / ceil(n_waves) reaches 85% of the best,
+ * n_waves = m_blocks * splits / num_cus, searched up to min(128, num_cus,
+ * max_selected_blocks); one split when the m-blocks already fill 80% of the
+ * machine or there are at most 4 blocks).  One (batch, KV head) pair is one
+ * m-block.  Returns a value >= 1, or 0 when an argument is out of range.
+ */
+int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,
+                             int num_cus);
+
+/* Workspace for bsattn_decode_gqa: fp32 partial outputs [B, Hq, splits, D]
+ * and their base-2 log-sum-exp [B, Hq, splits], 256-byte aligned.  Returns 0
+ * when an argument is out of range. */
+size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/*
+ * Split-KV sparse GQA decode over packed variable-length KV (same guide,
+ * §6, §6.1, §6.2), one query token per sequence.
+ *   q            : bfloat16 [B, Hq, D]
+ *   k, v         : bfloat16 [total_k, Hkv, D], sequence b occupies rows
+ *                  cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   cu_seqlens_k : int32 [B + 1], nondecreasing, cu[0] = 0, cu[B] <= total_k
+ *   block_indices: int32 [B, Hkv, max_selected_blocks]; entry i selects
+ *                  tokens [64 i, min(64 i + 64, len_b)) of the sequence; -1
+ *                  (or any i < 0 or i >= ceil(len_b / 64)) selects nothing.
+ *                  Order does not matter; duplicates are not allowed.
+ *   out          : bfloat16 [B, Hq, D]
+ * Query head hq reads KV head hq / (Hq / Hkv) (consecutive query heads share
+ * a KV head).  out = softmax(q . k_t / sqrt(D)) V over the selected tokens;
+ * zeros when nothing is selected.  The slot list of each (batch, KV head) is
+ * cut into num_splits contiguous ranges (the first (slots mod splits) ranges
+ * one slot longer); each range yields a partial output and a log-sum-exp,
+ * and a second kernel merges them with weights 2^(lse - max lse).
+ * num_splits <= 0 uses bsattn_decode_num_splits with the device's CU count.
+ * A sequence whose cu_seqlens_k range is decreasing or ends beyond total_k
+ * is treated as empty.
+ * Errors: NULL pointers; B, Hq, Hkv, max_selected_blocks, total_k <= 0,
+ * Hq % Hkv != 0, num_splits > max_selected_blocks (SHAPE); D not 64 or 128,
+ * or Hq / Hkv > 16 (UNSUPPORTED); workspace smaller than
+ * bsattn_decode_workspace_bytes for the split count used (WORKSPACE).
+ */
+bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* cu_seqlens_k, const int32_t* block_indices, int B,
+                                int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
+                                int num_splits, uint16_t* out, void* workspace,
+                                size_t workspace_bytes, bsattn_stream_t stream);
+
+/* The split count bsattn_decode_gqa would use for num_splits <= 0 on the
+ * current device (queries the CU count once per device). Returns 0 on error. */
+int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,118 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function the header declares, and rejects bad arguments on the host before
+any launch.  Also pins the library's split heuristic against the oracle's."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_amd as bsa
+from oracle import heuristic as oh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+
+def _lib():
+    if not os.path.exists(bsa.LIB_PATH):
+        pytest.skip("libbsattn.so not built (run __graft_entry__.build())")
+    return bsa.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert set(_declared()) == set(bsa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert bsa.bsattn_version().count(".") == 2
+    for s in range(6):
+        assert bsa.bsattn_status_string(s)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails validation first
+
+
+def test_mask_builders_validate_on_host():
+    lib = _lib()
+    assert lib.bsattn_build_mask_topk(None, 1, 1, 4, 2, 0, 1, FAKE, None) == 1
+    assert lib.bsattn_build_mask_topk(FAKE, 1, 1, 4, 5, 0, 1, FAKE, None) == 2   # topk > nb
+    assert lib.bsattn_build_mask_topk(FAKE, 1, 1, 4, -1, 0, 1, FAKE, None) == 2
+    assert lib.bsattn_build_mask_topk(FAKE, 0, 1, 4, 1, 0, 1, FAKE, None) == 2
+    assert lib.bsattn_build_mask_threshold(FAKE, 1, 1, 0, 0.5, 0, 1, FAKE, None) == 2
+    assert lib.bsattn_build_mask_threshold(FAKE, 1, 1, 4, 0.5, 0, 1, None, None) == 1
+    assert lib.bsattn_mask_to_indices(FAKE, 1, -1, 4, 1, FAKE, FAKE, None) == 2
+    assert lib.bsattn_mask_to_indices(FAKE, 1, 1, 4, 1, None, FAKE, None) == 1
+
+
+def test_fwd_validates_on_host():
+    lib = _lib()
+    F = FAKE
+    assert lib.bsattn_fwd(F, F, None, F, 1, 1, 64, 64, 1, F, None, 0, None) == 1
+    assert lib.bsattn_fwd(F, F, F, F, 1, 1, 0, 64, 1, F, None, 0, None) == 2
+    assert lib.bsattn_fwd(F, F, F, F, 1, 1, 64, 96, 1, F, None, 0, None) == 3
+    assert lib.bsattn_fwd(F, F, F, F, 1, 1, 64, 256, 1, F, None, 0, None) == 3
+    assert lib.bsattn_fwd_indices(F, F, F, None, F, 1, 1, 64, 64, 1, F, None) == 1
+    assert lib.bsattn_fwd_indices(F, F, F, F, F, 1, 1, 64, 32, 1, F, None) == 3
+    assert lib.bsattn_fwd_workspace_bytes(2, 16, 4096, 64) == 0
+
+
+def test_decode_validates_on_host():
+    lib = _lib()
+    F = FAKE
+    args = dict(B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2)
+
+    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2, ws=None, wsb=0):
+        return lib.bsattn_decode_gqa(q, F, F, cu, F, B, Hq, Hkv, D, ms, tk, ns, F, ws, wsb, None)
+
+    assert call(q=None) == 1
+    assert call(cu=None) == 1
+    assert call(Hq=6, Hkv=4) == 2          # Hq % Hkv
+    assert call(ns=5) == 2                 # more splits than slots
+    assert call(ms=0) == 2
+    assert call(tk=0) == 2
+    assert call(D=80) == 3
+    assert call(Hq=34, Hkv=2) == 3         # group of 17 query heads
+    assert call(ns=2) == 4                 # partials need a workspace
+    need = lib.bsattn_decode_workspace_bytes(2, 8, 128, 2)
+    assert need >= 2 * 8 * 2 * (128 + 1) * 4 and need % 256 == 0
+    assert call(ns=2, ws=F, wsb=need - 1) == 4
+    assert lib.bsattn_decode_workspace_bytes(2, 8, 128, 1) == 0    # one split writes the output directly
+    assert lib.bsattn_decode_workspace_bytes(0, 8, 128, 2) == 0
+
+
+def test_library_heuristic_matches_oracle_sweep():
+    _lib()
+    n = 0
+    for B in (1, 2, 3, 8, 16, 64):
+        for Hkv in (1, 2, 8):
+            for G in (1, 4, 16):
+                for ms in (1, 3, 4, 5, 17, 64, 200):
+                    for cus in (80, 132, 256, 304):
+                        want = oh.decode_num_splits(B, Hkv * G, Hkv, ms, 128, cus)
+                        got = bsa.bsattn_decode_num_splits(B, Hkv * G, Hkv, ms, 128, cus)
+                        assert got == want, (B, Hkv, G, ms, cus)
+                        n += 1
+    assert n > 1000
+    assert bsa.bsattn_decode_num_splits(8, 32, 8, 64, 128, 256) == 4
+    assert bsa.bsattn_decode_num_splits(8, 30, 8, 64, 128, 256) == 0   # Hq % Hkv
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    _lib()
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    m = torch.ones((1, 1, 1, 1), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.bsattn_fwd(q, q, q, m)
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.bsattn_build_mask_topk(torch.zeros((1, 1, 2, 2)), 1)

@@ -1,0 +1,165 @@
+"""GPU parity: block-sparse prefill against the float64 oracle.
+
+Small configurations are compared on every output element; the large
+configurations run at full size in the launch configuration the benchmark
+uses and are compared on sampled rows the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import block_sparse_attention_amd as bsa
+from block_sparse_attention_amd import inputs as gen
+from oracle import attention as oa
+from oracle import mask as om
+from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _mask_for(cfg, scores):
+    if cfg.mask_kind == "topk":
+        return om.build_mask_topk(scores, cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
+    return om.build_mask_threshold(scores, cfg.threshold, cfg.dense_last_two_rows, cfg.force_diagonal)
+
+
+def _run_gpu(qkv, mask, causal):
+    q, k, v = (to_gpu_bf16(qkv[n]) for n in ("q", "k", "v"))
+    out = bsa.bsattn_fwd(q, k, v, to_gpu(mask), causal)
+    return gpu_bf16_to_f64(out)
+
+
+def _f64(qkv):
+    return {n: gen.bf16_bits_to_f64(qkv[n]) for n in ("q", "k", "v")}
+
+
+@pytest.mark.parametrize("name", ["P0", "P1", "C1", "C2"])
+def test_configs_every_element(name):
+    cfg = gen.CONFIGS[name]
+    inp = gen.prefill_inputs(cfg, 0)
+    mask = _mask_for(cfg, inp["scores"])
+    say(f"[prefill] {name} B{cfg.B} H{cfg.H} S{cfg.S} D{cfg.D} blocks={int(mask.sum())}")
+    got = _run_gpu(inp, mask, cfg.is_causal)
+    x = _f64(inp)
+    want = oa.prefill(x["q"], x["k"], x["v"], mask, cfg.is_causal)
+    check_close(got, want, name)
+
+
+def _sample_rows(S, nb, rng):
+    rows = {0, 1, 63, 64, 65, S // 2, S - 129, S - 65, S - 64, S - 1}
+    rows |= set(rng.integers(0, S, size=6).tolist())
+    return sorted(r for r in rows if 0 <= r < S)
+
+
+@pytest.mark.parametrize("name", ["C3", "C4"])
+def test_large_configs_sampled_rows(name):
+    cfg = gen.CONFIGS[name]
+    scores = gen.prefill_scores(cfg, 0)
+    mask = _mask_for(cfg, scores)
+    qkv = gen.prefill_qkv(cfg, 0)
+    say(f"[prefill] {name} full size B{cfg.B} H{cfg.H} S{cfg.S} D{cfg.D} blocks={int(mask.sum())}")
+    got = _run_gpu(qkv, mask, cfg.is_causal)
+    rng = np.random.default_rng(123)
+    heads = [(0, 0), (cfg.B - 1, cfg.H - 1)] + [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H))) for _ in range(2)]
+    g_rows, w_rows = [], []
+    for b, h in heads:
+        rows = _sample_rows(cfg.S, cfg.nb, rng)
+        q, k, v = (gen.bf16_bits_to_f64(qkv[n][b, h]) for n in ("q", "k", "v"))
+        w_rows.append(oa.prefill_head_rows(q, k, v, mask[b, h], cfg.is_causal, rows))
+        g_rows.append(got[b, h, rows])
+    check_close(np.concatenate(g_rows), np.concatenate(w_rows), f"{name} sampled rows")
+    assert np.isfinite(got).all()
+
+
+def _random_case(B, H, S, D, seed, density=0.4, causal=True, diag=True):
+    rng = np.random.default_rng(seed)
+    nb = -(-S // 64)
+    mask = (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
+    if diag:
+        mask[..., np.arange(nb), np.arange(nb)] = 1
+    qkv = {n: gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D), dtype=np.float32)) for n in ("q", "k", "v")}
+    return qkv, mask
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 200, 383])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_lengths(S, D, causal):
+    qkv, mask = _random_case(1, 3, S, D, seed=S * 10 + D + causal, causal=causal)
+    say(f"[prefill] ragged S={S} D={D} causal={causal}")
+    got = _run_gpu(qkv, mask, causal)
+    x = _f64(qkv)
+    check_close(got, oa.prefill(x["q"], x["k"], x["v"], mask, causal), f"S{S} D{D} c{causal}")
+
+
+@pytest.mark.parametrize("B,H", [(2, 4), (1, 8), (3, 5), (2, 16)])
+def test_head_counts_and_xcd_mapping(B, H):
+    # batch*heads a multiple of 8 takes the XCD-grouped issue order, otherwise the plain one
+    qkv, mask = _random_case(B, H, 320, 64, seed=B * 100 + H)
+    say(f"[prefill] B{B} H{H} S320")
+    got = _run_gpu(qkv, mask, True)
+    x = _f64(qkv)
+    check_close(got, oa.prefill(x["q"], x["k"], x["v"], mask, True), f"B{B}H{H}")
+
+
+def test_empty_rows_nonzero_bytes_and_dense():
+    qkv, mask = _random_case(1, 4, 256, 64, seed=5, diag=False)
+    mask[0, 0] = 0                      # a head with no block at all -> zeros
+    mask[0, 1, 2, :] = 0                # one empty query block
+    mask[0, 2] = np.tril(np.ones((4, 4), np.uint8)) * 7   # any nonzero byte selects; dense causal
+    mask[0, 3] = 1                      # upper blocks are ignored when causal
+    say("[prefill] empty rows / nonzero bytes / dense")
+    got = _run_gpu(qkv, mask, True)
+    x = _f64(qkv)
+    want = oa.prefill(x["q"], x["k"], x["v"], mask, True)
+    check_close(got, want, "special masks")
+    assert (got[0, 0] == 0).all()
+    assert (got[0, 1, 128:192] == 0).all()
+    # the dense head equals dense causal attention
+    import torch
+    import torch.nn.functional as F
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x[n][0, 2:3]) for n in ("q", "k", "v")),
+                                         is_causal=True).numpy()
+    check_close(got[0, 2:3], ref, "dense head vs SDPA")
+
+
+def test_noncausal_upper_blocks():
+    qkv, mask = _random_case(2, 2, 256, 128, seed=9, density=0.5, diag=False)
+    mask[..., 0, 3] = 1
+    say("[prefill] non-causal upper blocks D128")
+    got = _run_gpu(qkv, mask, False)
+    x = _f64(qkv)
+    check_close(got, oa.prefill(x["q"], x["k"], x["v"], mask, False), "non-causal")
+
+
+def test_indices_entry_matches_mask_entry_bitwise_and_is_deterministic():
+    qkv, mask = _random_case(2, 4, 448, 128, seed=11)
+    q, k, v = (to_gpu_bf16(qkv[n]) for n in ("q", "k", "v"))
+    m = to_gpu(mask)
+    say("[prefill] indices entry / determinism")
+    a = bsa.bsattn_fwd(q, k, v, m, True)
+    b = bsa.bsattn_fwd(q, k, v, m, True)
+    idx, cnt = bsa.bsattn_mask_to_indices(m, True)
+    c = bsa.bsattn_fwd_indices(q, k, v, idx, cnt, True)
+    import torch
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    # non-causal lists, including out-of-range entries, which are skipped
+    idx2, cnt2 = bsa.bsattn_mask_to_indices(m, False)
+    idx2[0, 0, 0, -1] = 999
+    cnt2[0, 0, 0] = 7
+    d = bsa.bsattn_fwd_indices(q, k, v, idx2, cnt2, False)
+    x = _f64(qkv)
+    want = oa.prefill(x["q"], x["k"], x["v"], mask, False)
+    check_close(gpu_bf16_to_f64(d), want, "indices non-causal")
+
+
+def test_c2_gpu_mask_drives_the_forward_pass():
+    # the whole hot path on device: scores -> mask -> forward, vs the oracle end to end
+    cfg = gen.CONFIGS["C1"]
+    inp = gen.prefill_inputs(cfg, 0)
+    say("[prefill] C1 device mask -> forward")
+    m = bsa.bsattn_build_mask_topk(to_gpu(inp["scores"]), cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
+    q, k, v = (to_gpu_bf16(inp[n]) for n in ("q", "k", "v"))
+    out = gpu_bf16_to_f64(bsa.bsattn_fwd(q, k, v, m, True))
+    mask = om.build_mask_topk(inp["scores"], cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
+    x = _f64(inp)
+    check_close(out, oa.prefill(x["q"], x["k"], x["v"], mask, True), "C1 end to end")
