@@ -71,6 +71,62 @@ __global__ __launch_bounds__(kTopkThreads) void mask_topk_kernel(const float* __
   }
 }
 
+// Order key of column c with score x: larger key <=> larger score, and among
+// equal scores the lower column.  -0.0 and +0.0 are equal scores.
+__device__ __forceinline__ uint64_t rank_key(float x, int c) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+}
+
+constexpr int kWaveRows = 4;        // rows per work-group, one wave each
+constexpr int kWaveMaxNb = 1024;    // rows up to this length use the one-wave kernel
+
+// One wave per score row: the row's order keys sit in LDS; lane owns columns
+// lane, lane+64, ... and counts the keys above each of its own.
+__global__ __launch_bounds__(kWaveRows * kWave) void mask_topk_wave_kernel(
+    const float* __restrict__ scores, int64_t rows, int nb, int topk, int dense2, int diag,
+    uint8_t* __restrict__ mask) {
+  __shared__ uint64_t keys[kWaveRows][kWaveMaxNb];
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * kWaveRows + w;
+  if (row >= rows) return;  // the whole wave leaves; only wave-level syncs below
+  const int i = (int)(row % nb);
+  const float* x = scores + row * (int64_t)nb;
+  uint8_t* out = mask + row * (int64_t)nb;
+
+  const bool dense_row = dense2 && i >= nb - 2;
+  if (dense_row || topk >= nb || topk == 0) {
+    const bool all = dense_row || topk >= nb;
+    for (int j = lane; j < nb; j += kWave) out[j] = ((j <= i) && (all || (diag && j == i))) ? 1 : 0;
+    return;
+  }
+  uint64_t* kr = keys[w];
+  for (int c = lane; c < nb; c += kWave) kr[c] = rank_key(x[c], c);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int j0 = 0; j0 < nb; j0 += kWave) {
+    const int j = j0 + lane;
+    if (j0 > i) {            // the whole group lies above the diagonal
+      if (j < nb) out[j] = 0;
+      continue;
+    }
+    const uint64_t kj = (j < nb) ? kr[j] : ~0ull;
+    int beat = 0;
+    for (int c = 0; c < nb; ++c) beat += kr[c] > kj;
+    if (j < nb) {
+      bool pick;
+      if (j > i) pick = false;
+      else if (diag && j == i) pick = true;
+      else pick = beat < topk;
+      out[j] = pick ? 1 : 0;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void mask_threshold_kernel(const float* __restrict__ scores,
                                                              int64_t total, int nb, float thr,
                                                              int dense2, int diag,
@@ -118,8 +174,14 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint8_t* __restrict_
 hipError_t launch_mask_topk(const float* scores, int B, int H, int nb, int topk, int dense2,
                             int diag, uint8_t* mask, hipStream_t stream) {
   const int64_t rows = (int64_t)B * H * nb;
-  hipLaunchKernelGGL(mask_topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), 0, stream,
-                     scores, nb, topk, dense2, diag, mask);
+  if (nb <= kWaveMaxNb) {
+    const int64_t blocks = (rows + kWaveRows - 1) / kWaveRows;
+    hipLaunchKernelGGL(mask_topk_wave_kernel, dim3((unsigned)blocks), dim3(kWaveRows * kWave), 0,
+                       stream, scores, rows, nb, topk, dense2, diag, mask);
+  } else {
+    hipLaunchKernelGGL(mask_topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), 0, stream,
+                       scores, nb, topk, dense2, diag, mask);
+  }
   return hipGetLastError();
 }
 

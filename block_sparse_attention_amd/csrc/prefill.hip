@@ -34,6 +34,7 @@ namespace bsattn {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr float kLazy = 8.0f;   // log2 headroom before the running max must move
 
 template <int D>
 struct Cfg {
@@ -183,20 +184,17 @@ prefill_kernel(PrefillArgs a, int map_mode, int group) {
   };
 
   u32x4 kr[C::kPerThread], vr[C::kPerThread];
+  // Rows past the end of the sequence read the last row instead (always in
+  // bounds); their scores are masked to -inf and, for V, zeroed, so the values
+  // never matter except that they must be finite.
   auto fetch = [&](int j) {
 #pragma unroll
     for (int t = 0; t < C::kPerThread; ++t) {
       const int chunk = tid + kThreads * t;
-      const int r = chunk / C::kRowChunks;
-      const int c8 = chunk % C::kRowChunks;
-      const int key = j * 64 + r;
-      if (key < S) {
-        kr[t] = *(const u32x4*)(K + (int64_t)key * D + c8 * 8);
-        vr[t] = *(const u32x4*)(V + (int64_t)key * D + c8 * 8);
-      } else {
-        kr[t] = u32x4{0, 0, 0, 0};
-        vr[t] = u32x4{0, 0, 0, 0};
-      }
+      const int key = min(j * 64 + chunk / C::kRowChunks, S - 1);
+      const int64_t off = (int64_t)key * D + (chunk % C::kRowChunks) * 8;
+      kr[t] = *(const u32x4*)(K + off);
+      vr[t] = *(const u32x4*)(V + off);
     }
   };
   auto stage = [&]() {
@@ -237,24 +235,38 @@ prefill_kernel(PrefillArgs a, int map_mode, int group) {
     // ---- causal diagonal block and ragged tail ----
     const int kbase = j * 64;
     if ((CAUSAL && j == i) || kbase + 64 > S) {
+      // keys of this block at or beyond `vis` are hidden from this lane's query row
+      int vis = S - kbase;
+      if (CAUSAL && j == i) vis = min(vis, qrow - kbase + 1);
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const int k0 = kbase + 8 * (ii >> 2) + 4 * h + (ii & 3);
-        const int k1 = k0 + 32;
-        if (k0 >= S || (CAUSAL && k0 > qrow)) s0[ii] = -INFINITY;
-        if (k1 >= S || (CAUSAL && k1 > qrow)) s1[ii] = -INFINITY;
+        const int k0 = 8 * (ii >> 2) + 4 * h + (ii & 3);
+        if (k0 >= vis) s0[ii] = -INFINITY;
+        if (k0 + 32 >= vis) s1[ii] = -INFINITY;
       }
     }
 
     // ---- online softmax (base 2) ----
+    // The running maximum m only serves as the exponent offset, so it is
+    // raised lazily: only when some row's block maximum exceeds it by more
+    // than kLazy (in log2 units) is m moved and o, l rescaled.  Until then
+    // probabilities may reach 2^kLazy, harmless in fp32 and bf16.
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int ii = 1; ii < 16; ++ii) mx = fmaxf(mx, fmaxf(s0[ii], s1[ii]));
     mx = max_with_half_swap(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);
-    const float mc = m_use * c;
+    if (wave_ballot((mx - m) * c > kLazy) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = fast_exp2((m - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) o[t][ii] *= alpha;
+      m = m_new;
+    }
+    const float mc = (m == -INFINITY) ? 0.0f : m * c;
     float rs = 0.0f;
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
@@ -262,12 +274,7 @@ prefill_kernel(PrefillArgs a, int map_mode, int group) {
       s1[ii] = fast_exp2(fmaf(s1[ii], c, -mc));
       rs += s0[ii] + s1[ii];
     }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int t = 0; t < C::kDT; ++t)
-#pragma unroll
-      for (int ii = 0; ii < 16; ++ii) o[t][ii] *= alpha;
+    l += rs;
 
     // ---- O^T += V^T . P^T : four 16-key steps ----
 #pragma unroll
