@@ -145,6 +145,9 @@ static bsattn_status fwd_common(const uint16_t* q, const uint16_t* k, const uint
   if (B <= 0 || H <= 0 || S <= 0) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
   if ((long long)B * H * nblocks(S) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  // block lists are held as 16-bit entries in LDS next to the K/V ring
+  if (nblocks(S) > 65535 || prefill_lds_bytes(D, nblocks(S)) > kMaxLdsBytes)
+    return BSATTN_ERR_UNSUPPORTED;
   if (!fits_elems((long double)B * H * S * D)) return BSATTN_ERR_SHAPE;
   PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;

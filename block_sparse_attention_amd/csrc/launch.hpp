@@ -26,6 +26,9 @@ struct PrefillArgs {
   int causal;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// LDS one forward work-group needs (K/V ring plus the block list).
+size_t prefill_lds_bytes(int D, int nb);
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 struct DecodeArgs {
   const uint16_t* q;

@@ -15,16 +15,25 @@
 //   64 keys, so the row max / row sum are in-lane reductions plus a single
 //   permlane32 swap, and the exponentiated scores are already laid out as the
 //   B operand of O^T = V^T . P^T (no LDS round trip for P).
-// * K and V tiles are staged in LDS with a padded row stride; Q^T stays in
-//   registers; V^T operands come from ds_read_b64_tr_b16 transposed reads.
-// * The next active block's K/V are fetched into registers while the current
-//   block is computed.
-// * The mask row is compacted on the fly: a 64-column ballot per step gives
-//   the ascending list of selected key blocks, consumed bit by bit.
+// * Software pipeline over the active blocks t = 0, 1, ...: while the VALU
+//   works on the softmax of block t, the matrix cores run P.V of block t-1
+//   and Q.K^T of block t+1, so each wave keeps both pipes busy instead of
+//   alternating between them.
+// * The mask row is compacted once, at the start, into a list of key blocks
+//   in LDS (64-column ballots); the one block that needs in-block masking
+//   (the causal diagonal or the ragged tail) is put last.
+// * K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no
+//   registers) into two-slot rings, one block ahead, with explicit vmcnt
+//   waits.  Rows are XOR-swizzled in 16-byte granules so the K reads
+//   (ds_read_b128) and the transposed V reads (ds_read_b64_tr_b16) are free
+//   of bank conflicts; every LDS address is a per-lane constant plus an
+//   immediate.
 // * Work items are issued heaviest-first (last query block first), and when
 //   batch*heads is a multiple of 8 each head's items stay on one XCD so its
 //   K/V stay in that XCD's L2.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -38,59 +47,51 @@ constexpr float kLazy = 8.0f;   // log2 headroom before the running max must mov
 
 template <int D>
 struct Cfg {
-  static constexpr int kStride = D + 16;              // LDS row stride (bf16 elements)
-  static constexpr int kRowChunks = D / 8;            // 16-byte chunks per row
-  static constexpr int kPerThread = 64 * kRowChunks / kThreads;
-  static constexpr int kSteps = D / 16;               // k-steps of S^T = K . Q^T
-  static constexpr int kDT = D / 32;                  // 32-row tiles of O^T
+  static constexpr int G = D / 8;                       // 16-byte granules per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = 64 * kRowBytes;     // one K or V tile
+  static constexpr int kTileInstr = kTileBytes / 1024;  // 1 KiB wave-wide DMAs per tile
+  static constexpr int kWaveInstr = kTileInstr / 2;     // per wave, per tile
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;
+  static constexpr int kRingBytes = 4 * kTileBytes;     // K slots 0, 1, then V slots 0, 1
+  static constexpr int kSteps = D / 16;                 // k-steps of S^T = K . Q^T
+  static constexpr int kDT = D / 32;                    // 32-row tiles of O^T
 };
 
-// Active key blocks of one query-block row, read from the mask row.
-struct MaskRowIter {
-  const uint8_t* row;
-  int lim;
-  int c0;
-  uint64_t bits;
-  __device__ __forceinline__ void init(const uint8_t* r, int l) {
-    row = r;
-    lim = l;
-    c0 = -kWave;
-    bits = 0;
-  }
-  __device__ __forceinline__ int next() {
-    while (bits == 0) {
-      c0 += kWave;
-      if (c0 >= lim) return -1;
-      const int j = c0 + lane_id();
-      bits = wave_ballot(j < lim && row[j] != 0);
-    }
-    const int t = __builtin_ctzll(bits);
-    bits &= bits - 1;
-    return c0 + t;
-  }
-};
+// 16-byte granule swizzles: logical granule g of tile row r is stored at
+// granule g ^ swz(r).  K's depends on r & 15 only, V's on r & 3 only.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 64 ? (r & 2) : ((r & 3) << 1);
+}
 
-// Active key blocks of one row, read from a precomputed list.
-struct ListIter {
-  const int32_t* list;
-  int n;
-  int pos;
-  int lim;
-  __device__ __forceinline__ void init(const int32_t* l, int count, int lim_) {
-    list = l;
-    n = count;
-    pos = 0;
-    lim = lim_;
-  }
-  __device__ __forceinline__ int next() {
-    while (pos < n) {
-      const int j = __builtin_amdgcn_readfirstlane(list[pos]);
-      ++pos;
-      if (j >= 0 && j < lim) return j;
-    }
-    return -1;
-  }
-};
+// One wave-wide 16-byte-per-lane load straight into LDS: lane l reads
+// base + voff_l (base uniform, voff a per-lane byte offset) and its 16 bytes
+// go to LDS byte address lds + kLdsOff + 16 * l (M0 holds the uniform base).
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds), "i"(kLdsOff)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void barrier_raw() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Work item L -> (batch*head, query block).  Query blocks are issued last
 // first.  In mode 1 (batch*heads divisible by 8) item L runs on XCD L % 8;
@@ -120,20 +121,46 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(p));
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t byte_addr) {
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(uintptr_t)byte_addr);
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, bool CAUSAL, bool LIST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
-prefill_kernel(PrefillArgs a, int map_mode, int group) {
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t byte_addr) {
+  return *(const BSATTN_LDS u32x4*)(uintptr_t)byte_addr;
+}
+
+// Calls f(integral_constant<int, K>) for K = 0, 1, ... in order.
+template <class F, int... Ks>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Ks...>, F&& f) {
+  (f(std::integral_constant<int, Ks>{}), ...);
+}
+
+template <int D>
+size_t lds_bytes(int nb) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * C::kStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * C::kStride];
+  // the K/V rings, then the block list (nb entries + its length), 16-byte aligned
+  return (size_t)C::kRingBytes + (size_t)(((nb + 1) * 2 + 15) / 16) * 16;
+}
+
+// S^T of one block for one wave: keys 0..31 and 32..63, the wave's 32 query rows.
+struct Scores {
+  f32x16 s[2];
+};
+// P^T of one block as bf16 B operands of the four 16-key P.V steps.
+struct Probs {
+  u32x4 p[4];
+};
+
+template <int D, bool CAUSAL, bool LIST>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int map_mode, int group) {
+  using C = Cfg<D>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  uint16_t* list = (uint16_t*)(smem + C::kRingBytes);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
   const int h = lane >> 5;   // which half of the key rows / k-group this lane holds
   const int n = lane & 31;   // query row within the wave
@@ -149,15 +176,116 @@ prefill_kernel(PrefillArgs a, int map_mode, int group) {
   const uint16_t* __restrict__ V = a.v + head_off;
   const int q0 = i * 64;
   const int qrow = q0 + 32 * w + n;
+  const int lim = CAUSAL ? min(i + 1, nb) : nb;
+  // The one key block that needs masking inside the block: the causal
+  // diagonal, or without causality the ragged last block; -1 for none.
+  const int special = CAUSAL ? i : ((S % 64) ? nb - 1 : -1);
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds row qrow, dims 16s + 8h .. +8.
   u32x4 qf[C::kSteps];
+  {
+    const int qr = min(qrow, S - 1);   // rows past the end are never stored
 #pragma unroll
-  for (int s = 0; s < C::kSteps; ++s) {
-    if (qrow < S)
-      qf[s] = *(const u32x4*)(Q + (int64_t)qrow * D + 16 * s + 8 * h);
-    else
-      qf[s] = u32x4{0, 0, 0, 0};
+    for (int s = 0; s < C::kSteps; ++s)
+      qf[s] = *(const u32x4*)(Q + (int64_t)qr * D + 16 * s + 8 * h);
+  }
+
+  // ---- compact this query block's mask row (or list) into LDS ----
+  // Unmasked blocks first, in the order found; the special block last.
+  if (w == 0) {
+    int count = 0;
+    bool has_special = false;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    if constexpr (LIST) {
+      const int64_t row = (int64_t)bh * nb + i;
+      const int nl = max(0, min(a.cnt[row], nb));
+      const int32_t* src = a.idx + row * nb;
+      for (int c0 = 0; c0 < nl; c0 += kWave) {
+        const int p = c0 + lane;
+        const int j = p < nl ? src[p] : -1;
+        const bool sel = j >= 0 && j < lim;
+        const bool ok = sel && j != special;
+        const uint64_t bits = wave_ballot(ok);
+        if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
+        count += __popcll(bits);
+        has_special |= wave_ballot(sel && j == special) != 0;
+      }
+    } else {
+      const uint8_t* mrow = a.mask + ((int64_t)bh * nb + i) * nb;
+      for (int c0 = 0; c0 < lim; c0 += kWave) {
+        const int j = c0 + lane;
+        const bool sel = j < lim && mrow[j] != 0;
+        const bool ok = sel && j != special;
+        const uint64_t bits = wave_ballot(ok);
+        if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
+        count += __popcll(bits);
+        has_special |= wave_ballot(sel && j == special) != 0;
+      }
+    }
+    if (lane == 0) {
+      if (has_special) list[count++] = (uint16_t)special;
+      list[nb] = (uint16_t)count;   // the slot after the list holds its length
+    }
+  }
+  __syncthreads();
+  const int nblk = __builtin_amdgcn_readfirstlane((int)list[nb]);
+
+  // ---- per-lane DMA source byte offsets for this wave's share of a tile ----
+  // Instruction kk covers tile rows kk*kRowsPerInstr .. +kRowsPerInstr-1; lane l
+  // fills stored granule l % G of row kk*kRowsPerInstr + l / G.
+  uint32_t dma_k[C::kWaveInstr], dma_v[C::kWaveInstr];
+  int dma_r[C::kWaveInstr];
+#pragma unroll
+  for (int q = 0; q < C::kWaveInstr; ++q) {
+    const int kk = w + 2 * q;
+    const int r = kk * C::kRowsPerInstr + lane / C::G;
+    const int sg = lane % C::G;
+    dma_r[q] = r;
+    dma_k[q] = (uint32_t)((r * D + (sg ^ swz_k<D>(r)) * 8) * 2);
+    dma_v[q] = (uint32_t)((r * D + (sg ^ swz_v<D>(r)) * 8) * 2);
+  }
+  const uint32_t wbase = lds0 + (uint32_t)w * 1024;   // this wave's instructions: kk = w + 2q
+  // Load this wave's share of key block j's K (or V) tile into ring slot kSlot.
+  auto issue = [&](auto slot_c, auto is_v, int jv) {
+    constexpr uint32_t kSlot = decltype(slot_c)::value;
+    constexpr bool kV = decltype(is_v)::value;
+    const int j = __builtin_amdgcn_readfirstlane(jv);
+    const uint16_t* base = (kV ? V : K) + (int64_t)j * 64 * D;
+    const int last = S - 1 - j * 64;
+    if (last >= 63) {
+#pragma unroll
+      for (int q = 0; q < C::kWaveInstr; ++q)
+        dma16<kSlot>(base, kV ? dma_v[q] : dma_k[q], wbase + q * 2048);
+    } else {
+      // ragged last block: rows past the end re-read the last row (masked later)
+#pragma unroll
+      for (int q = 0; q < C::kWaveInstr; ++q) {
+        const uint32_t back = (uint32_t)(max(dma_r[q] - last, 0) * D * 2);
+        dma16<kSlot>(base, (kV ? dma_v[q] : dma_k[q]) - back, wbase + q * 2048);
+      }
+    }
+  };
+  using K0 = std::integral_constant<uint32_t, 0 * C::kTileBytes>;
+  using K1 = std::integral_constant<uint32_t, 1 * C::kTileBytes>;
+  using V0 = std::integral_constant<uint32_t, 2 * C::kTileBytes>;
+  using V1 = std::integral_constant<uint32_t, 3 * C::kTileBytes>;
+  using IsK = std::false_type;
+  using IsV = std::true_type;
+
+  // ---- per-lane LDS read addresses (bytes, slot 0 of the ring) ----
+  uint32_t koff[C::kSteps];
+#pragma unroll
+  for (int st = 0; st < C::kSteps; ++st)
+    koff[st] = lds0 + (uint32_t)((n * C::G + ((2 * st + h) ^ swz_k<D>(n))) * 16);
+  const int tr_r = (lane >> 2) & 3;
+  const int tr_m = lane & 3;
+  const int tr_g = (lane >> 4) & 1;
+  uint32_t voff[C::kDT];
+#pragma unroll
+  for (int t = 0; t < C::kDT; ++t) {
+    const int gran = 4 * t + 2 * tr_g + (tr_m >> 1);
+    voff[t] = lds0 + (uint32_t)(((4 * h + tr_r) * C::G + (gran ^ swz_v<D>(tr_r))) * 16 +
+                                (tr_m & 1) * 8);
   }
 
   f32x16 o[C::kDT];
@@ -167,134 +295,257 @@ prefill_kernel(PrefillArgs a, int map_mode, int group) {
   float l = 0.0f;
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
 
-  const int lim = CAUSAL ? min(i + 1, nb) : nb;
-  MaskRowIter mit;
-  ListIter lit;
-  if constexpr (LIST) {
-    const int64_t row = (int64_t)bh * nb + i;
-    int count = a.cnt[row];
-    count = max(0, min(count, nb));
-    lit.init(a.idx + row * nb, count, lim);
-  } else {
-    mit.init(a.mask + ((int64_t)bh * nb + i) * nb, lim);
-  }
-  auto next_block = [&]() -> int {
-    if constexpr (LIST) return lit.next();
-    else return mit.next();
-  };
-
-  u32x4 kr[C::kPerThread], vr[C::kPerThread];
-  // Rows past the end of the sequence read the last row instead (always in
-  // bounds); their scores are masked to -inf and, for V, zeroed, so the values
-  // never matter except that they must be finite.
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int t = 0; t < C::kPerThread; ++t) {
-      const int chunk = tid + kThreads * t;
-      const int key = min(j * 64 + chunk / C::kRowChunks, S - 1);
-      const int64_t off = (int64_t)key * D + (chunk % C::kRowChunks) * 8;
-      kr[t] = *(const u32x4*)(K + off);
-      vr[t] = *(const u32x4*)(V + off);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int t = 0; t < C::kPerThread; ++t) {
-      const int chunk = tid + kThreads * t;
-      const int r = chunk / C::kRowChunks;
-      const int c8 = chunk % C::kRowChunks;
-      *(u32x4*)(Ks + r * C::kStride + c8 * 8) = kr[t];
-      *(u32x4*)(Vs + r * C::kStride + c8 * 8) = vr[t];
-    }
-  };
-
-  // lane coordinates for the transposed V reads
-  const int tr_r = (lane >> 2) & 3;
-  const int tr_m = lane & 3;
-  const int tr_g = (lane >> 4) & 1;
-
-  int j = next_block();
-  if (j >= 0) fetch(j);
-  while (j >= 0) {
-    __syncthreads();  // every wave is done with the previous tile
-    stage();
-    __syncthreads();
-    const int jn = next_block();
-    if (jn >= 0) fetch(jn);  // in flight while this block is computed
-
-    // ---- S^T = K . Q^T : two 32-key tiles ----
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // ---- the phases of one block ----
+  // S^T of the block whose K tile sits in slot kSlot.
+  auto qk = [&](auto slot_c, Scores& sc) {
+    constexpr uint32_t kSlot = decltype(slot_c)::value;
+    sc.s[0] = f32x16{};
+    sc.s[1] = f32x16{};
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
-      const u32x4 a0 = *(const u32x4*)(Ks + n * C::kStride + 16 * st + 8 * h);
-      const u32x4 a1 = *(const u32x4*)(Ks + (32 + n) * C::kStride + 16 * st + 8 * h);
-      s0 = mfma32(a0, qf[st], s0);
-      s1 = mfma32(a1, qf[st], s1);
+      const u32x4 a0 = lds_read_b128(koff[st] + kSlot);
+      const u32x4 a1 = lds_read_b128(koff[st] + kSlot + 32 * C::G * 16);
+      sc.s[0] = mfma32(a0, qf[st], sc.s[0]);
+      sc.s[1] = mfma32(a1, qf[st], sc.s[1]);
     }
-
-    // ---- causal diagonal block and ragged tail ----
-    const int kbase = j * 64;
-    if ((CAUSAL && j == i) || kbase + 64 > S) {
-      // keys of this block at or beyond `vis` are hidden from this lane's query row
-      int vis = S - kbase;
-      if (CAUSAL && j == i) vis = min(vis, qrow - kbase + 1);
+  };
+  // O^T += V^T . P^T for the block whose V tile sits in slot kSlot.
+  auto pv = [&](auto slot_c, const Probs& pr) {
+    constexpr uint32_t kSlot = decltype(slot_c)::value;
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        const int k0 = 8 * (ii >> 2) + 4 * h + (ii & 3);
-        if (k0 >= vis) s0[ii] = -INFINITY;
-        if (k0 + 32 >= vis) s1[ii] = -INFINITY;
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int tt = 0; tt < C::kDT; ++tt) {
+        const uint32_t a0 = voff[tt] + kSlot + (16 * u) * C::G * 16;
+        const u32x2 lo = lds_read_tr16(a0);
+        const u32x2 hi = lds_read_tr16(a0 + 8 * C::G * 16);
+        o[tt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pr.p[u], o[tt]);
       }
     }
-
-    // ---- online softmax (base 2) ----
-    // The running maximum m only serves as the exponent offset, so it is
-    // raised lazily: only when some row's block maximum exceeds it by more
-    // than kLazy (in log2 units) is m moved and o, l rescaled.  Until then
-    // probabilities may reach 2^kLazy, harmless in fp32 and bf16.
-    float mx = fmaxf(s0[0], s1[0]);
+  };
+  // In-block masking of key block j: keys past the end, and keys after the
+  // query row on the causal diagonal, get -inf.
+  auto mask_block = [&](int j, Scores& sc) {
+    const int kbase = j * 64;
+    int vis = S - kbase;
+    if (CAUSAL && j == i) vis = min(vis, qrow - kbase + 1);
 #pragma unroll
-    for (int ii = 1; ii < 16; ++ii) mx = fmaxf(mx, fmaxf(s0[ii], s1[ii]));
+    for (int ii = 0; ii < 16; ++ii) {
+      const int k0 = 8 * (ii >> 2) + 4 * h + (ii & 3);
+      if (k0 >= vis) sc.s[0][ii] = -INFINITY;
+      if (k0 + 32 >= vis) sc.s[1][ii] = -INFINITY;
+    }
+  };
+  // Softmax of one block: row maximum, P = 2^(S c - m c) as bf16 B operands
+  // of P.V, and the row sums.  The running max m only serves as the exponent
+  // offset, so it is moved lazily: the exponentials are first taken against
+  // the current m (no dependency on this block's max, so they overlap the
+  // matrix work), and only when some row's block maximum exceeds m by more
+  // than kLazy (log2 units) is m raised, o and l rescaled and the block's
+  // exponentials taken again.  Until then probabilities may reach 2^kLazy,
+  // harmless in fp32 and bf16; a first pass against a stale m can overflow
+  // only when the redo is taken, which discards it.
+  auto exps = [&](const Scores& sc, Probs& pr, float mc) -> float {
+    float rs = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x16& sp = sc.s[u >> 1];
+      const int base = 8 * (u & 1);
+      float e[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        e[k] = fast_exp2(fmaf(sp[base + k], c, -mc));
+        rs += e[k];
+      }
+      pr.p[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                      pack_bf16x2(e[6], e[7])};
+    }
+    return rs;
+  };
+  // Instruction order for one pipelined iteration: LDS reads feed the 32x32
+  // MFMAs, and the softmax VALU work is spread between them so the matrix
+  // cores and the VALU run side by side.
+  auto interleave = [&]() {
+    constexpr int kMfma = 4 * C::kDT + 2 * C::kSteps;            // P.V + Q.K^T
+    constexpr int kReads = 8 * C::kDT + 2 * C::kSteps;           // tr16 reads + b128 reads
+    constexpr int kValuPer = (D == 64) ? 8 : 4;
+#pragma unroll
+    for (int k = 0; k < kMfma; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + kMfma - 1) / kMfma, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);                     // VALU
+    }
+  };
+
+  auto softmax = [&](const Scores& sc, Probs& pr, auto pipelined) {
+    float mx = fmaxf(sc.s[0][0], sc.s[1][0]);
+#pragma unroll
+    for (int ii = 1; ii < 16; ++ii) mx = fmaxf(mx, fmaxf(sc.s[0][ii], sc.s[1][ii]));
     mx = max_with_half_swap(mx);
+    float rs = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
+    if constexpr (decltype(pipelined)::value) interleave();
+    // keep the first pass ahead of the redo test (it would otherwise be sunk
+    // into the not-taken path and lose its overlap with the matrix work)
+    asm volatile("" ::"v"(pr.p[0]), "v"(pr.p[1]), "v"(pr.p[2]), "v"(pr.p[3]), "v"(rs));
     if (wave_ballot((mx - m) * c > kLazy) != 0) {
       const float m_new = fmaxf(m, mx);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
       const float alpha = fast_exp2((m - m_use) * c);
       l *= alpha;
 #pragma unroll
-      for (int t = 0; t < C::kDT; ++t)
+      for (int tt = 0; tt < C::kDT; ++tt)
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) o[t][ii] *= alpha;
+        for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
       m = m_new;
-    }
-    const float mc = (m == -INFINITY) ? 0.0f : m * c;
-    float rs = 0.0f;
-#pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-      s0[ii] = fast_exp2(fmaf(s0[ii], c, -mc));
-      s1[ii] = fast_exp2(fmaf(s1[ii], c, -mc));
-      rs += s0[ii] + s1[ii];
+      rs = exps(sc, pr, m_use * c);
     }
     l += rs;
-
-    // ---- O^T += V^T . P^T : four 16-key steps ----
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x16& sp = (u < 2) ? s0 : s1;
-      const int base = 8 * (u & 1);
-      const u32x4 pb = u32x4{pack_bf16x2(sp[base + 0], sp[base + 1]),
-                             pack_bf16x2(sp[base + 2], sp[base + 3]),
-                             pack_bf16x2(sp[base + 4], sp[base + 5]),
-                             pack_bf16x2(sp[base + 6], sp[base + 7])};
-      const int row0 = 16 * u + 4 * h + tr_r;
-#pragma unroll
-      for (int t = 0; t < C::kDT; ++t) {
-        const int col = 32 * t + 16 * tr_g + 4 * tr_m;
-        const u32x2 lo = lds_read_tr16(Vs + row0 * C::kStride + col);
-        const u32x2 hi = lds_read_tr16(Vs + (row0 + 8) * C::kStride + col);
-        o[t] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[t]);
-      }
+  };
+  // ---- software pipeline over the list ----
+  // Block t's K tile goes to K slot t&1 and its V tile to V slot t&1.
+  // Iteration t: wait + barrier (K_{t+1}, V_{t-1} landed; every wave is done
+  // with K_t and V_{t-2}); load V_t and K_{t+2}; then
+  //   P.V of block t-1 | row max of block t | Q.K^T of block t+1 | exp of block t.
+  Scores sa, sb;
+  Probs pa, pb;
+  if (nblk > 0) {
+    issue(K0{}, IsK{}, list[0]);
+    issue(V0{}, IsV{}, list[0]);
+    if (nblk > 1) {
+      issue(K1{}, IsK{}, list[1]);
+      wait_vmem<2 * C::kWaveInstr>();   // K_0 landed (V_0 and K_1 may still be in flight)
+    } else {
+      wait_vmem<C::kWaveInstr>();
     }
-    j = jn;
+    barrier_raw();
+    qk(K0{}, sa);
+  }
+
+  // One steady-state iteration, 1 <= t <= nblk - 2 (block t needs no masking).
+  // Hand-ordered as kSlots MFMA slots, each
+  //   { LDS operand read for slot k+2 ; MFMA k ; softmax slice k },
+  // fenced so the compiler keeps the order: the matrix cores run P.V of
+  // block t-1 and Q.K^T of block t+1 while the VALU takes the exponentials
+  // of block t (against the current running max; see softmax above).
+  constexpr int kPvMfma = 4 * C::kDT;        // u-major, tile-minor
+  constexpr int kQkMfma = 2 * C::kSteps;     // step-major, tile-minor
+  constexpr int kSlots = kPvMfma + kQkMfma;  // 16 at D = 64, 32 at D = 128
+  constexpr int kPerSlot = 32 / kSlots;      // score elements per lane per slot
+  auto steady = [&](auto kt, auto kn, auto vt, auto vp, int t, Scores& s_cur, Scores& s_next,
+                    const Probs& p_prev, Probs& p_cur) {
+    constexpr uint32_t kN = decltype(kn)::value;
+    constexpr uint32_t kVP = decltype(vp)::value;
+    wait_vmem<0>();
+    barrier_raw();
+    issue(vt, IsV{}, list[t]);
+    if (t + 2 < nblk) issue(kt, IsK{}, list[t + 2]);
+
+    u32x4 op[kSlots];
+    auto read = [&](auto k_c) {
+      constexpr int k = decltype(k_c)::value;
+      if constexpr (k < kPvMfma) {
+        constexpr int u = k / C::kDT, tt = k % C::kDT;
+        const uint32_t a0 = voff[tt] + kVP + (16 * u) * C::G * 16;
+        const u32x2 lo = lds_read_tr16(a0);
+        const u32x2 hi = lds_read_tr16(a0 + 8 * C::G * 16);
+        op[k] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        constexpr int kk = k - kPvMfma, st = kk / 2, tile = kk % 2;
+        op[k] = lds_read_b128(koff[st] + kN + tile * 32 * C::G * 16);
+      }
+    };
+    auto mfma = [&](auto k_c) {
+      constexpr int k = decltype(k_c)::value;
+      if constexpr (k < kPvMfma) {
+        constexpr int u = k / C::kDT, tt = k % C::kDT;
+        o[tt] = mfma32(op[k], p_prev.p[u], o[tt]);
+      } else {
+        constexpr int kk = k - kPvMfma, st = kk / 2, tile = kk % 2;
+        s_next.s[tile] = mfma32(op[k], qf[st], s_next.s[tile]);
+      }
+    };
+    const float mc = (m == -INFINITY) ? 0.0f : m * c;
+    float mx = -INFINITY, rs = 0.0f;
+    float pe[32];
+    auto valu = [&](auto k_c) {
+      constexpr int k = decltype(k_c)::value;
+      static_for(std::make_integer_sequence<int, kPerSlot>{}, [&](auto q_c) {
+        constexpr int e = k * kPerSlot + decltype(q_c)::value;
+        const float x = s_cur.s[e >> 4][e & 15];
+        mx = fmaxf(mx, x);
+        pe[e] = fast_exp2(fmaf(x, c, -mc));
+        rs += pe[e];
+        if constexpr (e & 1) p_cur.p[e >> 3][(e >> 1) & 3] = pack_bf16x2(pe[e - 1], pe[e]);
+      });
+    };
+    s_next.s[0] = f32x16{};
+    s_next.s[1] = f32x16{};
+    read(std::integral_constant<int, 0>{});
+    read(std::integral_constant<int, 1>{});
+    static_for(std::make_integer_sequence<int, kSlots>{}, [&](auto k_c) {
+      constexpr int k = decltype(k_c)::value;
+      if constexpr (k + 2 < kSlots) read(std::integral_constant<int, k + 2>{});
+      mfma(k_c);
+      valu(k_c);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    mx = max_with_half_swap(mx);
+    // keep the first pass ahead of the redo test
+    asm volatile("" ::"v"(p_cur.p[0]), "v"(p_cur.p[1]), "v"(p_cur.p[2]), "v"(p_cur.p[3]), "v"(rs));
+    if (wave_ballot((mx - m) * c > kLazy) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = fast_exp2((m - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < C::kDT; ++tt)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
+      m = m_new;
+      rs = exps(s_cur, p_cur, m_use * c);
+    }
+    l += rs;
+  };
+  // The last iteration, t = nblk - 1 >= 1 (block t may need masking).
+  auto last = [&](auto vt, auto vp, int t, Scores& s_cur, const Probs& p_prev, Probs& p_cur) {
+    const int j = __builtin_amdgcn_readfirstlane((int)list[t]);
+    wait_vmem<0>();
+    barrier_raw();
+    issue(vt, IsV{}, list[t]);
+    pv(vp, p_prev);
+    if (j == special) mask_block(j, s_cur);
+    softmax(s_cur, p_cur, std::false_type{});
+    wait_vmem<0>();
+    barrier_raw();
+    pv(vt, p_cur);
+  };
+
+  if (nblk > 1) {
+    // t = 0: no P.V yet
+    wait_vmem<0>();
+    barrier_raw();
+    if (2 < nblk) issue(K0{}, IsK{}, list[2]);
+    qk(K1{}, sb);
+    softmax(sa, pa, std::false_type{});
+    int t = 1;
+    for (; t + 2 <= nblk - 1; t += 2) {
+      steady(K1{}, K0{}, V1{}, V0{}, t, sb, sa, pa, pb);       // t odd
+      steady(K0{}, K1{}, V0{}, V1{}, t + 1, sa, sb, pb, pa);   // t + 1 even
+    }
+    if (t == nblk - 2) {
+      steady(K1{}, K0{}, V1{}, V0{}, t, sb, sa, pa, pb);       // t odd
+      ++t;
+    }
+    // t == nblk - 1: its scores are in sb when t is odd, in sa when even
+    if (t & 1) last(V1{}, V0{}, t, sb, pa, pb);
+    else last(V0{}, V1{}, t, sa, pb, pa);
+  } else if (nblk == 1) {
+    const int j = __builtin_amdgcn_readfirstlane((int)list[0]);
+    if (j == special) mask_block(j, sa);
+    softmax(sa, pa, std::false_type{});
+    wait_vmem<0>();
+    barrier_raw();
+    pv(V0{}, pa);
   }
 
   // ---- normalise and store ----
@@ -327,13 +578,23 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     while (per_xcd % g) --g;
     group = g;
   }
+  const size_t lds = lds_bytes<D>(a.nb);
+  auto kern = prefill_kernel<D, CAUSAL, LIST>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int64_t items = (int64_t)BH * a.nb;
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, LIST>), dim3((unsigned)items), dim3(kThreads), 0,
-                     stream, a, mode, group);
+  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kThreads), lds, stream, a, mode, group);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t prefill_lds_bytes(int D, int nb) {
+  return D == 64 ? lds_bytes<64>(nb) : lds_bytes<128>(nb);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const bool list = a.mask == nullptr;
