@@ -10,15 +10,19 @@
 // hq / (Hq / Hkv).
 //
 // CDNA4 mapping (not the guide's kernel design):
-// * one work-group of 4 wave64s per (batch, KV head, split); the waves take
-//   the range's slots round-robin and are combined through LDS at the end;
+// * one work-group of 8 wave64s per (batch, KV head, split), two waves per
+//   SIMD; the waves take the range's slots round-robin and are combined
+//   through LDS at the end;
 // * per 64-token block, S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
 //   group's query heads as the 16 columns (K rows loaded straight from HBM
 //   into the A-operand layout, 16 bytes per lane);
 // * the exponentiated scores are already the B operand of O^T = V^T . P^T;
 //   V goes through LDS, read transposed with ds_read_b64_tr_b16;
-// * all K and V loads of a block are issued before any of its math, so each
-//   wave keeps 2 * 64 * D * 2 bytes in flight.
+// * software pipeline per wave: the next selected block's K loads are issued
+//   right after the current block's S^T, its V loads right after the current
+//   block's P.V, so a block's loads are in flight during the previous block's
+//   softmax and P.V.  Rows past the sequence end are clamped to its last row
+//   (no branches around loads) and masked in the scores.
 #include <math.h>
 
 #include "common.hpp"
@@ -28,7 +32,7 @@ namespace bsattn {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -47,6 +51,24 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Buffer resource over one 64-token block of one KV head: loads at byte
+// offsets past `bytes` return zero instead of touching memory, which is how
+// rows past the sequence end are kept out of the block.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+// voff is range-checked against the resource; soff is a small constant
+// added on top (kept within the row that voff addresses).
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 template <int D>
 struct DCfg {
   static constexpr int kStride = D + 16;     // LDS row stride of a V half tile
@@ -54,7 +76,19 @@ struct DCfg {
   static constexpr int kDT = D / 16;         // 16-row tiles of O^T
   static constexpr int kRowChunks = D / 8;   // 16-byte chunks per token row
   static constexpr int kVPer = 64 * kRowChunks / kWave;  // V chunks per lane per block
+  static constexpr int kTokPerInstr = kWave / kRowChunks;  // V tokens per load instruction
   static constexpr int kWaveLds = 32 * kStride;          // bf16 elements per wave
+  // the combine reuses a wave's region as floats: 16 m, 16 l, 16 x D o
+  static_assert(kWaveLds * 2 >= (32 + 16 * D) * 4, "combine area");
+};
+
+template <int D>
+struct KTile {
+  u32x4 f[4][D / 32];
+};
+template <int D>
+struct VTile {
+  u32x4 f[DCfg<D>::kVPer];
 };
 
 template <int D>
@@ -68,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int ns = a.num_splits;
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;     // query column of the 16x16 tiles
   const int grp = lane >> 4;     // k-group / row group
@@ -80,15 +114,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int len = (end >= start && end <= a.total_k && start >= 0) ? end - start : 0;
   const int nbb = (len + 63) / 64;
 
-  // this split's slot range
+  // this split's slot range; this wave takes slots my_start + w + kWaves * j
   const int nslots = a.max_sel;
   const int bps = nslots / ns;
   const int rem = nslots % ns;
   const int my_len = bps + (sid < rem ? 1 : 0);
   const int my_start = bps * sid + min(sid, rem);
+  const int nper = my_len > w ? (my_len - w + kWaves - 1) / kWaves : 0;
 
-  const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive tokens
+  const uint32_t rsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+
+  const int32_t* idx_row = a.block_indices + ((int64_t)b * a.Hkv + kvh) * nslots;
 
   // Q^T as the B operand: column col = query head kvh*G + col (zero when col >= G).
   u32x4 qf[C::kSteps];
@@ -109,51 +146,52 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   float m = -INFINITY;
   float l = 0.0f;
 
-  const int32_t* idx_row = a.block_indices + ((int64_t)b * a.Hkv + kvh) * nslots;
   const int tr_r = (lane >> 2) & 3;
   const int tr_m = lane & 3;
 
-  for (int slot = my_start + w; slot < my_start + my_len; slot += kWaves) {
-    const int blk = __builtin_amdgcn_readfirstlane(idx_row[slot]);
-    if (blk < 0 || blk >= nbb) continue;
-    const int tok0 = blk * 64;
-    const int ntok = min(64, len - tok0);
-    const uint16_t* __restrict__ Kp = a.k + ((int64_t)start + tok0) * row_stride + (int64_t)kvh * D;
-    const uint16_t* __restrict__ Vp = a.v + ((int64_t)start + tok0) * row_stride + (int64_t)kvh * D;
+  // per-lane byte offsets inside a block: K rows 16*tt + col, k-chunks
+  // 32*s + 8*grp (A-operand layout); V chunk lane + 64*t = (token, 16 bytes)
+  uint32_t koff[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) koff[tt] = (uint32_t)(16 * tt + col) * rsb + 16u * grp;
+  const uint32_t voff0 = (uint32_t)(lane / C::kRowChunks) * rsb + 16u * (lane % C::kRowChunks);
+  const uint32_t vstep = (uint32_t)C::kTokPerInstr * rsb;
 
-    // issue every load of the block first
-    u32x4 kf[4][C::kSteps];
+  auto rsrc = [&](const uint16_t* p, int blk) {
+    const int ntok = min(64, len - blk * 64);
+    const uint16_t* base = p + ((int64_t)start + (int64_t)blk * 64) * (rsb / 2) + (int64_t)kvh * D;
+    return block_rsrc(base, (uint32_t)(ntok - 1) * rsb + D * 2);
+  };
+  auto load_k = [&](int blk, KTile<D>& kt) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.k, blk);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 16 * tt + col;
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        if (tok < ntok)
-          kf[tt][s] = *(const u32x4*)(Kp + tok * row_stride + 32 * s + 8 * grp);
-        else
-          kf[tt][s] = u32x4{0, 0, 0, 0};
-      }
-    }
-    u32x4 vr[C::kVPer];
+      for (int s = 0; s < C::kSteps; ++s) kt.f[tt][s] = bload16(r, koff[tt], 64u * s);
+  };
+  auto load_v = [&](int blk, VTile<D>& vt) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.v, blk);
+    // recomputed per block (not hoisted): one offset register instead of kVPer
+    uint32_t vo = voff0;
+    asm volatile("" : "+v"(vo));
 #pragma unroll
-    for (int t = 0; t < C::kVPer; ++t) {
-      const int chunk = lane + kWave * t;
-      const int tok = chunk / C::kRowChunks;
-      const int c8 = chunk % C::kRowChunks;
-      if (tok < ntok)
-        vr[t] = *(const u32x4*)(Vp + tok * row_stride + c8 * 8);
-      else
-        vr[t] = u32x4{0, 0, 0, 0};
-    }
+    for (int t = 0; t < C::kVPer; ++t) vt.f[t] = bload16(r, vo + vstep * t, 0);
+  };
 
+  // one selected block: S^T, softmax, O^T += V^T . P^T; with MORE, the next
+  // block's K loads go out after S^T and its V loads after P.V
+  auto process = [&](int blk, int nblk, KTile<D>& kt, VTile<D>& vt, auto more_c) {
+    constexpr bool kMore = decltype(more_c)::value;
+    const int ntok = min(64, len - blk * 64);
     // S^T tiles: token 16*tt + 4*grp + r, query column col
     f32x4 sc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       sc[tt] = f32x4{};
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) sc[tt] = mfma16(kf[tt][s], qf[s], sc[tt]);
+      for (int s = 0; s < C::kSteps; ++s) sc[tt] = mfma16(kt.f[tt][s], qf[s], sc[tt]);
     }
+    if constexpr (kMore) load_k(nblk, kt);
     if (ntok < 64) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -183,6 +221,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
       }
     l = l * alpha + rs;
     m = m_new;
+    // P^T as the B operand of the two 32-token halves
+    u32x4 pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      pb[u] = u32x4{pack_bf16x2(sc[2 * u][0], sc[2 * u][1]),
+                    pack_bf16x2(sc[2 * u][2], sc[2 * u][3]),
+                    pack_bf16x2(sc[2 * u + 1][0], sc[2 * u + 1][1]),
+                    pack_bf16x2(sc[2 * u + 1][2], sc[2 * u + 1][3])};
 #pragma unroll
     for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
@@ -197,25 +243,47 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
         const int chunk = lane + kWave * (t + u * (C::kVPer / 2));
         const int tok = chunk / C::kRowChunks - 32 * u;
         const int c8 = chunk % C::kRowChunks;
-        *(u32x4*)(Vs + tok * C::kStride + c8 * 8) = vr[t + u * (C::kVPer / 2)];
+        *(u32x4*)(Vs + tok * C::kStride + c8 * 8) = vt.f[t + u * (C::kVPer / 2)];
       }
       wave_lds_sync();
-      const u32x4 pb = u32x4{pack_bf16x2(sc[2 * u][0], sc[2 * u][1]),
-                             pack_bf16x2(sc[2 * u][2], sc[2 * u][3]),
-                             pack_bf16x2(sc[2 * u + 1][0], sc[2 * u + 1][1]),
-                             pack_bf16x2(sc[2 * u + 1][2], sc[2 * u + 1][3])};
       const int row0 = 4 * grp + tr_r;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t) {
         const int cc = 16 * t + 4 * tr_m;
         const u32x2 lo = lds_read_tr16(Vs + row0 * C::kStride + cc);
         const u32x2 hi = lds_read_tr16(Vs + (row0 + 16) * C::kStride + cc);
-        o[t] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[t]);
+        o[t] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[t]);
       }
     }
+    if constexpr (kMore) load_v(nblk, vt);
+  };
+
+  for (int c0 = 0; c0 < nper; c0 += kWave) {
+    // this wave's next 64 slots: lane j holds slot my_start + w + kWaves * (c0 + j)
+    int bv = -1;
+    if (c0 + lane < nper) bv = idx_row[my_start + w + kWaves * (c0 + lane)];
+    uint64_t vm = wave_ballot(bv >= 0 && bv < nbb);
+    const int n = __builtin_popcountll(vm);
+    if (n == 0) continue;
+    auto take = [&]() {
+      const int j = __builtin_ctzll(vm);
+      vm &= vm - 1;
+      return __builtin_amdgcn_readlane(bv, j);
+    };
+    KTile<D> kt;
+    VTile<D> vt;
+    int blk = take();
+    load_k(blk, kt);
+    load_v(blk, vt);
+    for (int i = 1; i < n; ++i) {
+      const int nblk = take();
+      process(blk, nblk, kt, vt, BoolC<true>{});
+      blk = nblk;
+    }
+    process(blk, 0, kt, vt, BoolC<false>{});
   }
 
-  // ---- combine the four waves of this split ----
+  // ---- combine the waves of this split ----
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   wave_lds_sync();
@@ -260,7 +328,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   }
 }
 
-// One work-group per (batch, query head): weights 2^(lse_s - max lse).
+// One work-group per (batch, query head): weights 2^(lse_s - max lse),
+// accumulated in one pass with a running maximum so the loads of all splits
+// are independent of each other.
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int64_t bq = blockIdx.x;
@@ -268,16 +338,21 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int d = threadIdx.x;
   const float* lse = a.lse + bq * ns;
   const float* op = a.o_part + bq * ns * D;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[s]);
-  float num = 0.0f, den = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const float ls = lse[s];
-      const float wt = (ls == -INFINITY) ? 0.0f : fast_exp2(ls - M);
-      den += wt;
-      num += wt * op[(int64_t)s * D + d];
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) {
+    const float ls = lse[s];
+    const float x = op[(int64_t)s * D + d];
+    if (ls == -INFINITY) continue;
+    if (ls > M) {
+      const float sc = (M == -INFINITY) ? 0.0f : fast_exp2(M - ls);
+      num *= sc;
+      den *= sc;
+      M = ls;
     }
+    const float wt = fast_exp2(ls - M);
+    den += wt;
+    num += wt * x;
   }
   a.out[bq * D + d] = float_to_bf16_bits(den > 0.0f ? num / den : 0.0f);
 }

@@ -104,3 +104,26 @@ def test_deterministic():
     a = _gpu(inp, 4)
     b = _gpu(inp, 4)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_workspace_needs_no_clearing():
+    """Workspace contents left by anything (garbage, earlier calls, another
+    split count) must not change the result."""
+    cfg = gen.CONFIGS["P2"]
+    inp = gen.decode_inputs(cfg, 2)
+    want = _oracle(inp)
+    q, k, v = (to_gpu_bf16(inp[n]) for n in ("q", "k", "v"))
+    cu, idx = to_gpu(inp["cu_seqlens_k"]), to_gpu(inp["block_indices"])
+    big = bsa.bsattn_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.D, cfg.max_selected_blocks)
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill, ns in ((0xFF, 4), (None, 4), (0x00, 4), (None, 7), (None, 4), (0x5A, 2)):
+        if fill is not None:
+            ws.fill_(fill)
+        say(f"[decode] workspace fill={fill} ns={ns}")
+        o = bsa.bsattn_decode_gqa(q, k, v, cu, idx, num_splits=ns, workspace=ws)
+        outs.append(gpu_bf16_to_f64(o))
+        check_close(outs[-1], want, f"ws fill={fill} ns={ns}")
+    # the same split count gives bit-identical results whatever the workspace held
+    for i in (1, 2, 4):
+        np.testing.assert_array_equal(outs[i], outs[0])
