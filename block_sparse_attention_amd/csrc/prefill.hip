@@ -43,7 +43,6 @@ namespace bsattn {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr float kLazy = 8.0f;   // log2 headroom before the running max must move
 
 template <int D>
 struct Cfg {
@@ -336,69 +335,68 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
       if (k0 + 32 >= vis) sc.s[1][ii] = -INFINITY;
     }
   };
-  // Softmax of one block: row maximum, P = 2^(S c - m c) as bf16 B operands
-  // of P.V, and the row sums.  The running max m only serves as the exponent
-  // offset, so it is moved lazily: the exponentials are first taken against
-  // the current m (no dependency on this block's max, so they overlap the
-  // matrix work), and only when some row's block maximum exceeds m by more
-  // than kLazy (log2 units) is m raised, o and l rescaled and the block's
-  // exponentials taken again.  Until then probabilities may reach 2^kLazy,
-  // harmless in fp32 and bf16; a first pass against a stale m can overflow
-  // only when the redo is taken, which discards it.
+  // Softmax of one block: P = 2^(S c - m c) packed to bf16 B operands of
+  // P.V, and the row sum taken over the packed values with v_dot2 (two per
+  // instruction, and the same values P.V multiplies).  The running max m
+  // only serves as the exponent offset, so it is moved lazily: a block's
+  // exponentials are first taken against the current m, and only when some
+  // lane's 32-term partial sum exceeds 2^8 (so some probability may have
+  // reached that size) is m raised to the row maxima, o and l rescaled and
+  // the block's exponentials taken again.  A first pass against a stale m
+  // can overflow only when the redo is taken, which discards it.  The first
+  // block of an item sets m from its row maxima directly.
+  constexpr float kLazySum = 256.0f;   // 2^8
+  const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1)
+  auto dot_sum = [&](uint32_t pk, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, ones), acc, false);
+  };
   auto exps = [&](const Scores& sc, Probs& pr, float mc) -> float {
     float rs = 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const f32x16& sp = sc.s[u >> 1];
       const int base = 8 * (u & 1);
-      float e[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        e[k] = fast_exp2(fmaf(sp[base + k], c, -mc));
-        rs += e[k];
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pk = pack_bf16x2(fast_exp2(fmaf(sp[base + 2 * k], c, -mc)),
+                                        fast_exp2(fmaf(sp[base + 2 * k + 1], c, -mc)));
+        pr.p[u][k] = pk;
+        rs = dot_sum(pk, rs);
       }
-      pr.p[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                      pack_bf16x2(e[6], e[7])};
     }
     return rs;
   };
-  // Instruction order for one pipelined iteration: LDS reads feed the 32x32
-  // MFMAs, and the softmax VALU work is spread between them so the matrix
-  // cores and the VALU run side by side.
-  auto interleave = [&]() {
-    constexpr int kMfma = 4 * C::kDT + 2 * C::kSteps;            // P.V + Q.K^T
-    constexpr int kReads = 8 * C::kDT + 2 * C::kSteps;           // tr16 reads + b128 reads
-    constexpr int kValuPer = (D == 64) ? 8 : 4;
-#pragma unroll
-    for (int k = 0; k < kMfma; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, (kReads + kMfma - 1) / kMfma, 0);  // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);                     // VALU
-    }
-  };
-
-  auto softmax = [&](const Scores& sc, Probs& pr, auto pipelined) {
+  auto row_max = [&](const Scores& sc) {
     float mx = fmaxf(sc.s[0][0], sc.s[1][0]);
 #pragma unroll
     for (int ii = 1; ii < 16; ++ii) mx = fmaxf(mx, fmaxf(sc.s[0][ii], sc.s[1][ii]));
-    mx = max_with_half_swap(mx);
+    return max_with_half_swap(mx);
+  };
+  // Raise m to the block's row maxima, rescale o and l, redo the exponentials.
+  auto raise = [&](const Scores& sc, Probs& pr) -> float {
+    const float m_new = fmaxf(m, row_max(sc));
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = fast_exp2((m - m_use) * c);
+    l *= alpha;
+#pragma unroll
+    for (int tt = 0; tt < C::kDT; ++tt)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
+    m = m_new;
+    return exps(sc, pr, m_use * c);
+  };
+  // First block of an item: m = row max.
+  auto softmax_first = [&](const Scores& sc, Probs& pr) {
+    m = row_max(sc);
+    l = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
+  };
+  // Any later block, outside the pipelined loop.
+  auto softmax = [&](const Scores& sc, Probs& pr) {
     float rs = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
-    if constexpr (decltype(pipelined)::value) interleave();
-    // keep the first pass ahead of the redo test (it would otherwise be sunk
-    // into the not-taken path and lose its overlap with the matrix work)
+    // keep the first pass ahead of the redo test
     asm volatile("" ::"v"(pr.p[0]), "v"(pr.p[1]), "v"(pr.p[2]), "v"(pr.p[3]), "v"(rs));
-    if (wave_ballot((mx - m) * c > kLazy) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2((m - m_use) * c);
-      l *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < C::kDT; ++tt)
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
-      m = m_new;
-      rs = exps(sc, pr, m_use * c);
-    }
+    if (wave_ballot(rs > kLazySum) != 0) rs = raise(sc, pr);
     l += rs;
   };
   // ---- software pipeline over the list ----
@@ -431,6 +429,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   constexpr int kQkMfma = 2 * C::kSteps;     // step-major, tile-minor
   constexpr int kSlots = kPvMfma + kQkMfma;  // 16 at D = 64, 32 at D = 128
   constexpr int kPerSlot = 32 / kSlots;      // score elements per lane per slot
+#ifndef BSATTN_AHEAD
+#define BSATTN_AHEAD 2
+#endif
+  constexpr int kAhead = BSATTN_AHEAD;       // LDS operand reads issued this many slots ahead
   auto steady = [&](auto kt, auto kn, auto vt, auto vp, int t, Scores& s_cur, Scores& s_next,
                     const Probs& p_prev, Probs& p_cur) {
     constexpr uint32_t kN = decltype(kn)::value;
@@ -465,45 +467,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
       }
     };
     const float mc = (m == -INFINITY) ? 0.0f : m * c;
-    float mx = -INFINITY, rs = 0.0f;
+    float rs = 0.0f;
     float pe[32];
     auto valu = [&](auto k_c) {
       constexpr int k = decltype(k_c)::value;
       static_for(std::make_integer_sequence<int, kPerSlot>{}, [&](auto q_c) {
         constexpr int e = k * kPerSlot + decltype(q_c)::value;
-        const float x = s_cur.s[e >> 4][e & 15];
-        mx = fmaxf(mx, x);
-        pe[e] = fast_exp2(fmaf(x, c, -mc));
-        rs += pe[e];
-        if constexpr (e & 1) p_cur.p[e >> 3][(e >> 1) & 3] = pack_bf16x2(pe[e - 1], pe[e]);
+        pe[e] = fast_exp2(fmaf(s_cur.s[e >> 4][e & 15], c, -mc));
+        if constexpr (e & 1) {
+          const uint32_t pk = pack_bf16x2(pe[e - 1], pe[e]);
+          p_cur.p[e >> 3][(e >> 1) & 3] = pk;
+          rs = dot_sum(pk, rs);
+        }
       });
     };
     s_next.s[0] = f32x16{};
     s_next.s[1] = f32x16{};
-    read(std::integral_constant<int, 0>{});
-    read(std::integral_constant<int, 1>{});
+    static_for(std::make_integer_sequence<int, kAhead>{}, [&](auto k_c) { read(k_c); });
     static_for(std::make_integer_sequence<int, kSlots>{}, [&](auto k_c) {
       constexpr int k = decltype(k_c)::value;
-      if constexpr (k + 2 < kSlots) read(std::integral_constant<int, k + 2>{});
+      if constexpr (k + kAhead < kSlots) read(std::integral_constant<int, k + kAhead>{});
       mfma(k_c);
       valu(k_c);
       __builtin_amdgcn_sched_barrier(0);
     });
-    mx = max_with_half_swap(mx);
     // keep the first pass ahead of the redo test
     asm volatile("" ::"v"(p_cur.p[0]), "v"(p_cur.p[1]), "v"(p_cur.p[2]), "v"(p_cur.p[3]), "v"(rs));
-    if (wave_ballot((mx - m) * c > kLazy) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2((m - m_use) * c);
-      l *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < C::kDT; ++tt)
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
-      m = m_new;
-      rs = exps(s_cur, p_cur, m_use * c);
-    }
+    if (wave_ballot(rs > kLazySum) != 0) rs = raise(s_cur, p_cur);
     l += rs;
   };
   // The last iteration, t = nblk - 1 >= 1 (block t may need masking).
@@ -514,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     issue(vt, IsV{}, list[t]);
     pv(vp, p_prev);
     if (j == special) mask_block(j, s_cur);
-    softmax(s_cur, p_cur, std::false_type{});
+    softmax(s_cur, p_cur);
     wait_vmem<0>();
     barrier_raw();
     pv(vt, p_cur);
@@ -526,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     barrier_raw();
     if (2 < nblk) issue(K0{}, IsK{}, list[2]);
     qk(K1{}, sb);
-    softmax(sa, pa, std::false_type{});
+    softmax_first(sa, pa);
     int t = 1;
     for (; t + 2 <= nblk - 1; t += 2) {
       steady(K1{}, K0{}, V1{}, V0{}, t, sb, sa, pa, pb);       // t odd
@@ -542,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   } else if (nblk == 1) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[0]);
     if (j == special) mask_block(j, sa);
-    softmax(sa, pa, std::false_type{});
+    softmax_first(sa, pa);
     wait_vmem<0>();
     barrier_raw();
     pv(V0{}, pa);
