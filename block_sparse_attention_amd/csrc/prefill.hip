@@ -9,16 +9,21 @@
 // the running sum at the end (§4.7).
 //
 // How it is mapped to CDNA4 (this is not the guide's kernel design):
-// * 128 threads = 2 wave64s per work item; wave w owns query rows 32w..32w+31.
+// * Two or four wave64s per work item.  Waves w and w^1 take query rows
+//   0..31 and 32..63.  With two waves (D = 64) each sees all 64 keys of a
+//   block; with four (D = 128) wave w also takes keys 32 (w >> 1) .. +31 only,
+//   the two key halves run as independent online softmaxes and are merged
+//   once per item through LDS.  Splitting the keys halves the per-wave
+//   registers (two waves per SIMD at D = 128 instead of one) without reading
+//   the K/V tiles from LDS more than once per query row.
 // * Scores are formed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16:
-//   the accumulator gives each lane ONE query row (lane % 32) and 32 of the
-//   64 keys, so the row max / row sum are in-lane reductions plus a single
-//   permlane32 swap, and the exponentiated scores are already laid out as the
-//   B operand of O^T = V^T . P^T (no LDS round trip for P).
+//   the accumulator gives each lane ONE query row (lane % 32) and 16 of the
+//   wave's 32 keys, so the row max / row sum are in-lane reductions plus a
+//   single permlane32 swap, and the exponentiated scores are already laid out
+//   as the B operand of O^T = V^T . P^T (no LDS round trip for P).
 // * Software pipeline over the active blocks t = 0, 1, ...: while the VALU
 //   works on the softmax of block t, the matrix cores run P.V of block t-1
-//   and Q.K^T of block t+1, so each wave keeps both pipes busy instead of
-//   alternating between them.
+//   and Q.K^T of block t+1.
 // * The mask row is compacted once, at the start, into a list of key blocks
 //   in LDS (64-column ballots); the one block that needs in-block masking
 //   (the causal diagonal or the ragged tail) is put last.
@@ -42,19 +47,29 @@ namespace bsattn {
 
 namespace {
 
-constexpr int kThreads = 128;
 
-template <int D>
+template <int KS>
+constexpr int kThreadsFor = 2 * KS * kWave;
+
+// KS: key splits per work item.  KS = 1: two waves, each 32 query rows x all
+// 64 keys of a block.  KS = 2: four waves, each 32 query rows x 32 keys.
+template <int D, int KS>
 struct Cfg {
+  static constexpr int kWaves = 2 * KS;
+  static constexpr int kThreads = kThreadsFor<KS>;
+  static constexpr int NT = 2 / KS;                     // 32-key score tiles per wave and block
   static constexpr int G = D / 8;                       // 16-byte granules per row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileBytes = 64 * kRowBytes;     // one K or V tile
   static constexpr int kTileInstr = kTileBytes / 1024;  // 1 KiB wave-wide DMAs per tile
-  static constexpr int kWaveInstr = kTileInstr / 2;     // per wave, per tile
+  static constexpr int kWaveInstr = kTileInstr / kWaves;  // per wave, per tile
   static constexpr int kRowsPerInstr = 1024 / kRowBytes;
   static constexpr int kRingBytes = 4 * kTileBytes;     // K slots 0, 1, then V slots 0, 1
   static constexpr int kSteps = D / 16;                 // k-steps of S^T = K . Q^T
   static constexpr int kDT = D / 32;                    // 32-row tiles of O^T
+  static constexpr int kXchgBytes = kDT / 2 * 16 * kWave * 4;  // o half-tiles one wave hands over
+  static_assert(KS == 1 || kWaves * kXchgBytes <= 2 * kTileBytes, "exchange fits the K slots");
+  static constexpr int kStatsBytes = KS == 2 ? kWaves * kWave * 8 : 0;
 };
 
 // 16-byte granule swizzles: logical granule g of tile row r is stored at
@@ -135,34 +150,46 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, Ks...>, F&
   (f(std::integral_constant<int, Ks>{}), ...);
 }
 
-template <int D>
+template <int D, int KS>
 size_t lds_bytes(int nb) {
-  using C = Cfg<D>;
-  // the K/V rings, then the block list (nb entries + its length), 16-byte aligned
-  return (size_t)C::kRingBytes + (size_t)(((nb + 1) * 2 + 15) / 16) * 16;
+  using C = Cfg<D, KS>;
+  // the K/V rings, the row statistics of the key-half merge (KS = 2: 4 waves
+  // x 64 lanes x 2 floats), then the block list (nb entries + its length),
+  // 16-byte aligned
+  return (size_t)C::kRingBytes + C::kStatsBytes + (size_t)(((nb + 1) * 2 + 15) / 16) * 16;
 }
 
-// S^T of one block for one wave: keys 0..31 and 32..63, the wave's 32 query rows.
+// S^T of one block for one wave: NT tiles of 32 keys x its 32 query rows.
+template <int NT>
 struct Scores {
-  f32x16 s[2];
+  f32x16 s[NT];
 };
-// P^T of one block as bf16 B operands of the four 16-key P.V steps.
+// P^T of one block as bf16 B operands of the wave's 2 NT 16-key P.V steps.
+template <int NT>
 struct Probs {
-  u32x4 p[4];
+  u32x4 p[2 * NT];
 };
 
-template <int D, bool CAUSAL, bool LIST>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int map_mode, int group) {
-  using C = Cfg<D>;
+template <int D, int KS, bool CAUSAL, bool LIST>
+__global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, int map_mode,
+                                                                  int group) {
+  using C = Cfg<D, KS>;
+  constexpr int kWaves = C::kWaves;
+  constexpr int NT = C::NT;
+  using Sc = Scores<NT>;
+  using Pr = Probs<NT>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  uint16_t* list = (uint16_t*)(smem + C::kRingBytes);
+  float* stats = (float*)(smem + C::kRingBytes);                    // [wave][m | l][lane]
+  uint16_t* list = (uint16_t*)(smem + C::kRingBytes + C::kStatsBytes);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int rg = w & 1;      // query rows 32 rg .. +31
+  const int kh = w >> 1;     // keys 32 NT kh .. +32 NT - 1 of every block
   const int lane = tid & 63;
   const int h = lane >> 5;   // which half of the key rows / k-group this lane holds
-  const int n = lane & 31;   // query row within the wave
+  const int n = lane & 31;   // query row within the wave's 32
 
   const int nb = a.nb;
   const int S = a.S;
@@ -174,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   const uint16_t* __restrict__ K = a.k + head_off;
   const uint16_t* __restrict__ V = a.v + head_off;
   const int q0 = i * 64;
-  const int qrow = q0 + 32 * w + n;
+  const int qrow = q0 + 32 * rg + n;
   const int lim = CAUSAL ? min(i + 1, nb) : nb;
   // The one key block that needs masking inside the block: the causal
   // diagonal, or without causality the ragged last block; -1 for none.
@@ -236,14 +263,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   int dma_r[C::kWaveInstr];
 #pragma unroll
   for (int q = 0; q < C::kWaveInstr; ++q) {
-    const int kk = w + 2 * q;
+    const int kk = w + kWaves * q;
     const int r = kk * C::kRowsPerInstr + lane / C::G;
     const int sg = lane % C::G;
     dma_r[q] = r;
     dma_k[q] = (uint32_t)((r * D + (sg ^ swz_k<D>(r)) * 8) * 2);
     dma_v[q] = (uint32_t)((r * D + (sg ^ swz_v<D>(r)) * 8) * 2);
   }
-  const uint32_t wbase = lds0 + (uint32_t)w * 1024;   // this wave's instructions: kk = w + 2q
+  const uint32_t wbase = lds0 + (uint32_t)w * 1024;   // this wave's instructions: kk = w + kWaves q
   // Load this wave's share of key block j's K (or V) tile into ring slot kSlot.
   auto issue = [&](auto slot_c, auto is_v, int jv) {
     constexpr uint32_t kSlot = decltype(slot_c)::value;
@@ -254,13 +281,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     if (last >= 63) {
 #pragma unroll
       for (int q = 0; q < C::kWaveInstr; ++q)
-        dma16<kSlot>(base, kV ? dma_v[q] : dma_k[q], wbase + q * 2048);
+        dma16<kSlot>(base, kV ? dma_v[q] : dma_k[q], wbase + q * kWaves * 1024);
     } else {
       // ragged last block: rows past the end re-read the last row (masked later)
 #pragma unroll
       for (int q = 0; q < C::kWaveInstr; ++q) {
         const uint32_t back = (uint32_t)(max(dma_r[q] - last, 0) * D * 2);
-        dma16<kSlot>(base, (kV ? dma_v[q] : dma_k[q]) - back, wbase + q * 2048);
+        dma16<kSlot>(base, (kV ? dma_v[q] : dma_k[q]) - back, wbase + q * kWaves * 1024);
       }
     }
   };
@@ -272,10 +299,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   using IsV = std::true_type;
 
   // ---- per-lane LDS read addresses (bytes, slot 0 of the ring) ----
+  // K rows of this wave's keys (tile tt adds 32 rows); V^T rows of its 16-key steps.
   uint32_t koff[C::kSteps];
 #pragma unroll
-  for (int st = 0; st < C::kSteps; ++st)
-    koff[st] = lds0 + (uint32_t)((n * C::G + ((2 * st + h) ^ swz_k<D>(n))) * 16);
+  for (int st = 0; st < C::kSteps; ++st) {
+    const int r = 32 * NT * kh + n;
+    koff[st] = lds0 + (uint32_t)((r * C::G + ((2 * st + h) ^ swz_k<D>(r))) * 16);
+  }
   const int tr_r = (lane >> 2) & 3;
   const int tr_m = lane & 3;
   const int tr_g = (lane >> 4) & 1;
@@ -283,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
 #pragma unroll
   for (int t = 0; t < C::kDT; ++t) {
     const int gran = 4 * t + 2 * tr_g + (tr_m >> 1);
-    voff[t] = lds0 + (uint32_t)(((4 * h + tr_r) * C::G + (gran ^ swz_v<D>(tr_r))) * 16 +
+    voff[t] = lds0 + (uint32_t)(((32 * NT * kh + 4 * h + tr_r) * C::G + (gran ^ swz_v<D>(tr_r))) *
+                                    16 +
                                 (tr_m & 1) * 8);
   }
 
@@ -296,23 +327,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
 
   // ---- the phases of one block ----
   // S^T of the block whose K tile sits in slot kSlot.
-  auto qk = [&](auto slot_c, Scores& sc) {
+  auto qk = [&](auto slot_c, Sc& sc) {
     constexpr uint32_t kSlot = decltype(slot_c)::value;
-    sc.s[0] = f32x16{};
-    sc.s[1] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < C::kSteps; ++st) {
-      const u32x4 a0 = lds_read_b128(koff[st] + kSlot);
-      const u32x4 a1 = lds_read_b128(koff[st] + kSlot + 32 * C::G * 16);
-      sc.s[0] = mfma32(a0, qf[st], sc.s[0]);
-      sc.s[1] = mfma32(a1, qf[st], sc.s[1]);
-    }
+    for (int tt = 0; tt < NT; ++tt) sc.s[tt] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        sc.s[tt] = mfma32(lds_read_b128(koff[st] + kSlot + tt * 32 * C::G * 16), qf[st], sc.s[tt]);
   };
   // O^T += V^T . P^T for the block whose V tile sits in slot kSlot.
-  auto pv = [&](auto slot_c, const Probs& pr) {
+  auto pv = [&](auto slot_c, const Pr& pr) {
     constexpr uint32_t kSlot = decltype(slot_c)::value;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * NT; ++u) {
 #pragma unroll
       for (int tt = 0; tt < C::kDT; ++tt) {
         const uint32_t a0 = voff[tt] + kSlot + (16 * u) * C::G * 16;
@@ -324,23 +353,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   };
   // In-block masking of key block j: keys past the end, and keys after the
   // query row on the causal diagonal, get -inf.
-  auto mask_block = [&](int j, Scores& sc) {
-    const int kbase = j * 64;
+  auto mask_block = [&](int j, Sc& sc) {
+    const int kbase = j * 64 + 32 * NT * kh;
     int vis = S - kbase;
     if (CAUSAL && j == i) vis = min(vis, qrow - kbase + 1);
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-      const int k0 = 8 * (ii >> 2) + 4 * h + (ii & 3);
-      if (k0 >= vis) sc.s[0][ii] = -INFINITY;
-      if (k0 + 32 >= vis) sc.s[1][ii] = -INFINITY;
-    }
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int k0 = 32 * tt + 8 * (ii >> 2) + 4 * h + (ii & 3);
+        if (k0 >= vis) sc.s[tt][ii] = -INFINITY;
+      }
   };
   // Softmax of one block: P = 2^(S c - m c) packed to bf16 B operands of
   // P.V, and the row sum taken over the packed values with v_dot2 (two per
   // instruction, and the same values P.V multiplies).  The running max m
   // only serves as the exponent offset, so it is moved lazily: a block's
   // exponentials are first taken against the current m, and only when some
-  // lane's 32-term partial sum exceeds 2^8 (so some probability may have
+  // lane's 16 NT-term partial sum exceeds 2^8 (so some probability may have
   // reached that size) is m raised to the row maxima, o and l rescaled and
   // the block's exponentials taken again.  A first pass against a stale m
   // can overflow only when the redo is taken, which discards it.  The first
@@ -351,10 +381,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
                                            __builtin_bit_cast(bf16x2, ones), acc, false);
   };
-  auto exps = [&](const Scores& sc, Probs& pr, float mc) -> float {
+  auto exps = [&](const Sc& sc, Pr& pr, float mc) -> float {
     float rs = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * NT; ++u) {
       const f32x16& sp = sc.s[u >> 1];
       const int base = 8 * (u & 1);
 #pragma unroll
@@ -367,14 +397,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     }
     return rs;
   };
-  auto row_max = [&](const Scores& sc) {
-    float mx = fmaxf(sc.s[0][0], sc.s[1][0]);
+  auto row_max = [&](const Sc& sc) {
+    float mx = sc.s[0][0];
 #pragma unroll
-    for (int ii = 1; ii < 16; ++ii) mx = fmaxf(mx, fmaxf(sc.s[0][ii], sc.s[1][ii]));
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int ii = (tt == 0 ? 1 : 0); ii < 16; ++ii) mx = fmaxf(mx, sc.s[tt][ii]);
     return max_with_half_swap(mx);
   };
   // Raise m to the block's row maxima, rescale o and l, redo the exponentials.
-  auto raise = [&](const Scores& sc, Probs& pr) -> float {
+  auto raise = [&](const Sc& sc, Pr& pr) -> float {
     const float m_new = fmaxf(m, row_max(sc));
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = fast_exp2((m - m_use) * c);
@@ -387,15 +419,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     return exps(sc, pr, m_use * c);
   };
   // First block of an item: m = row max.
-  auto softmax_first = [&](const Scores& sc, Probs& pr) {
+  auto softmax_first = [&](const Sc& sc, Pr& pr) {
     m = row_max(sc);
     l = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
   };
   // Any later block, outside the pipelined loop.
-  auto softmax = [&](const Scores& sc, Probs& pr) {
+  auto softmax = [&](const Sc& sc, Pr& pr) {
     float rs = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
     // keep the first pass ahead of the redo test
-    asm volatile("" ::"v"(pr.p[0]), "v"(pr.p[1]), "v"(pr.p[2]), "v"(pr.p[3]), "v"(rs));
+#pragma unroll
+    for (int u = 0; u < 2 * NT; ++u) asm volatile("" ::"v"(pr.p[u]));
+    asm volatile("" ::"v"(rs));
     if (wave_ballot(rs > kLazySum) != 0) rs = raise(sc, pr);
     l += rs;
   };
@@ -403,9 +437,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
   // Block t's K tile goes to K slot t&1 and its V tile to V slot t&1.
   // Iteration t: wait + barrier (K_{t+1}, V_{t-1} landed; every wave is done
   // with K_t and V_{t-2}); load V_t and K_{t+2}; then
-  //   P.V of block t-1 | row max of block t | Q.K^T of block t+1 | exp of block t.
-  Scores sa, sb;
-  Probs pa, pb;
+  //   P.V of block t-1 | Q.K^T of block t+1 | exp of block t.
+  Sc sa, sb;
+  Pr pa, pb;
   if (nblk > 0) {
     issue(K0{}, IsK{}, list[0]);
     issue(V0{}, IsV{}, list[0]);
@@ -421,20 +455,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
 
   // One steady-state iteration, 1 <= t <= nblk - 2 (block t needs no masking).
   // Hand-ordered as kSlots MFMA slots, each
-  //   { LDS operand read for slot k+2 ; MFMA k ; softmax slice k },
+  //   { LDS operand read for slot k+kAhead ; MFMA k ; softmax slice k },
   // fenced so the compiler keeps the order: the matrix cores run P.V of
   // block t-1 and Q.K^T of block t+1 while the VALU takes the exponentials
   // of block t (against the current running max; see softmax above).
-  constexpr int kPvMfma = 4 * C::kDT;        // u-major, tile-minor
-  constexpr int kQkMfma = 2 * C::kSteps;     // step-major, tile-minor
-  constexpr int kSlots = kPvMfma + kQkMfma;  // 16 at D = 64, 32 at D = 128
-  constexpr int kPerSlot = 32 / kSlots;      // score elements per lane per slot
+  constexpr int kPvMfma = 2 * NT * C::kDT;   // u-major, tile-minor
+  constexpr int kQkMfma = NT * C::kSteps;    // step-major, tile-minor
+  constexpr int kSlots = kPvMfma + kQkMfma;
+  constexpr int kPerSlot = 16 * NT / kSlots; // score elements per lane per slot
+  static_assert(kPerSlot * kSlots == 16 * NT, "slices cover the block");
 #ifndef BSATTN_AHEAD
 #define BSATTN_AHEAD 2
 #endif
   constexpr int kAhead = BSATTN_AHEAD;       // LDS operand reads issued this many slots ahead
-  auto steady = [&](auto kt, auto kn, auto vt, auto vp, int t, Scores& s_cur, Scores& s_next,
-                    const Probs& p_prev, Probs& p_cur) {
+  auto steady = [&](auto kt, auto kn, auto vt, auto vp, int t, Sc& s_cur, Sc& s_next,
+                    const Pr& p_prev, Pr& p_cur) {
     constexpr uint32_t kN = decltype(kn)::value;
     constexpr uint32_t kVP = decltype(vp)::value;
     wait_vmem<0>();
@@ -452,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
         const u32x2 hi = lds_read_tr16(a0 + 8 * C::G * 16);
         op[k] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       } else {
-        constexpr int kk = k - kPvMfma, st = kk / 2, tile = kk % 2;
+        constexpr int kk = k - kPvMfma, st = kk / NT, tile = kk % NT;
         op[k] = lds_read_b128(koff[st] + kN + tile * 32 * C::G * 16);
       }
     };
@@ -462,13 +497,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
         constexpr int u = k / C::kDT, tt = k % C::kDT;
         o[tt] = mfma32(op[k], p_prev.p[u], o[tt]);
       } else {
-        constexpr int kk = k - kPvMfma, st = kk / 2, tile = kk % 2;
-        s_next.s[tile] = mfma32(op[k], qf[st], s_next.s[tile]);
+        constexpr int kk = k - kPvMfma, st = kk / NT, tile = kk % NT;
+        s_next.s[tile] = mfma32(op[k], qf[st], st == 0 ? f32x16{} : s_next.s[tile]);
       }
     };
     const float mc = (m == -INFINITY) ? 0.0f : m * c;
     float rs = 0.0f;
-    float pe[32];
+    float pe[16 * NT];
     auto valu = [&](auto k_c) {
       constexpr int k = decltype(k_c)::value;
       static_for(std::make_integer_sequence<int, kPerSlot>{}, [&](auto q_c) {
@@ -481,8 +516,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
         }
       });
     };
-    s_next.s[0] = f32x16{};
-    s_next.s[1] = f32x16{};
     static_for(std::make_integer_sequence<int, kAhead>{}, [&](auto k_c) { read(k_c); });
     static_for(std::make_integer_sequence<int, kSlots>{}, [&](auto k_c) {
       constexpr int k = decltype(k_c)::value;
@@ -492,12 +525,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
       __builtin_amdgcn_sched_barrier(0);
     });
     // keep the first pass ahead of the redo test
-    asm volatile("" ::"v"(p_cur.p[0]), "v"(p_cur.p[1]), "v"(p_cur.p[2]), "v"(p_cur.p[3]), "v"(rs));
+#pragma unroll
+    for (int u = 0; u < 2 * NT; ++u) asm volatile("" ::"v"(p_cur.p[u]));
+    asm volatile("" ::"v"(rs));
     if (wave_ballot(rs > kLazySum) != 0) rs = raise(s_cur, p_cur);
     l += rs;
   };
   // The last iteration, t = nblk - 1 >= 1 (block t may need masking).
-  auto last = [&](auto vt, auto vp, int t, Scores& s_cur, const Probs& p_prev, Probs& p_cur) {
+  auto last = [&](auto vt, auto vp, int t, Sc& s_cur, const Pr& p_prev, Pr& p_cur) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[t]);
     wait_vmem<0>();
     barrier_raw();
@@ -538,25 +573,95 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int ma
     pv(V0{}, pa);
   }
 
-  // ---- normalise and store ----
-  const float lt = sum_with_half_swap(l);
+  // ---- merge the two key halves of each row group, normalise and store ----
+  // Wave (rg, kh) finishes O^T tiles kh*kDT/2 .. +kDT/2-1 of its rows; it
+  // hands the other half of its tiles to its partner (rg, 1-kh) through the
+  // K slots of the ring (free: every wave passed a barrier after its last
+  // Q.K^T, and no K load is in flight) and its row max / row sum through
+  // `stats`.
+  if constexpr (KS == 1) {
+    // one wave holds the whole row: normalise and store
+    const float lt = sum_with_half_swap(l);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (qrow < S) {
+      uint16_t* __restrict__ O = a.out + head_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * t + 8 * g4 + 4 * h;
+          *(u32x2*)(O + d) = u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
+                                   pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
+        }
+    }
+  } else {
+  constexpr int kHalf = C::kDT / 2;
+  // KH: this wave's key half, as a compile-time value so o[] is indexed statically.
+  auto hand_over = [&](auto kh_c) {
+    constexpr int KH = decltype(kh_c)::value;
+    float* xout = (float*)(smem + w * C::kXchgBytes);
+#pragma unroll
+    for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) xout[(t * 16 + ii) * kWave + lane] = o[(1 - KH) * kHalf + t][ii];
+  };
+  if (kh == 0) hand_over(std::integral_constant<int, 0>{});
+  else hand_over(std::integral_constant<int, 1>{});
+  stats[w * 2 * kWave + lane] = m;
+  stats[w * 2 * kWave + kWave + lane] = sum_with_half_swap(l);
+  __syncthreads();
+  const int pw = w ^ 2;   // partner: same rows, other key half
+  const float* xin = (const float*)(smem + pw * C::kXchgBytes);
+  const float m_b = stats[pw * 2 * kWave + lane];
+  const float l_b = stats[pw * 2 * kWave + kWave + lane];
+  const float l_a = sum_with_half_swap(l);
+  const float M = fmaxf(m, m_b);
+  const float al_a = (m == -INFINITY) ? 0.0f : fast_exp2((m - M) * c);
+  const float al_b = (m_b == -INFINITY) ? 0.0f : fast_exp2((m_b - M) * c);
+  const float lt = l_a * al_a + l_b * al_b;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (qrow < S) {
+  const float fa = al_a * inv, fb = al_b * inv;
+  auto finish = [&](auto kh_c) {
+    constexpr int KH = decltype(kh_c)::value;
     uint16_t* __restrict__ O = a.out + head_off + (int64_t)qrow * D;
 #pragma unroll
-    for (int t = 0; t < C::kDT; ++t)
+    for (int t = 0; t < kHalf; ++t) {
+      constexpr int kBase = KH * kHalf;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * t + 8 * g4 + 4 * h;
-        const u32x2 val = u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
-                                pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
-        *(u32x2*)(O + d) = val;
+        float r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = 4 * g4 + e;
+          r4[e] = o[kBase + t][ii] * fa + xin[(t * 16 + ii) * kWave + lane] * fb;
+        }
+        const int d = 32 * (kBase + t) + 8 * g4 + 4 * h;
+        *(u32x2*)(O + d) = u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
       }
+    }
+  };
+  if (qrow < S) {
+    if (kh == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
+  }
   }
 }
 
+// Key splits per work item by head dim: at D = 64 two waves (all keys each)
+// keep the per-item overhead lowest; at D = 128 four waves (half the keys
+// each) halve the per-wave registers, so two waves fit per SIMD.
+#ifndef BSATTN_KS64
+#define BSATTN_KS64 1
+#endif
+#ifndef BSATTN_KS128
+#define BSATTN_KS128 2
+#endif
+template <int D>
+constexpr int kKeySplits = D == 64 ? BSATTN_KS64 : BSATTN_KS128;
+
 template <int D, bool CAUSAL, bool LIST>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int KS = kKeySplits<D>;
   const int BH = a.B * a.H;
   int mode = 0, group = 1;
   if (BH % 8 == 0) {
@@ -568,22 +673,23 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     while (per_xcd % g) --g;
     group = g;
   }
-  const size_t lds = lds_bytes<D>(a.nb);
-  auto kern = prefill_kernel<D, CAUSAL, LIST>;
+  const size_t lds = lds_bytes<D, KS>(a.nb);
+  auto kern = prefill_kernel<D, KS, CAUSAL, LIST>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int64_t items = (int64_t)BH * a.nb;
-  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kThreads), lds, stream, a, mode, group);
+  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
+                     group);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t prefill_lds_bytes(int D, int nb) {
-  return D == 64 ? lds_bytes<64>(nb) : lds_bytes<128>(nb);
+  return D == 64 ? lds_bytes<64, kKeySplits<64>>(nb) : lds_bytes<128, kKeySplits<128>>(nb);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
