@@ -27,6 +27,11 @@ or >= ceil(len_b / BLOCK) select nothing.  KV is packed by ``cu_seqlens_k``.
 The split-KV partition and log-sum-exp merge of §6.1 are again only a
 re-association; ``merge_partials`` states that merge on its own so tests can
 pin it against the unsplit result.
+
+Two decode variants of the same guide change only which tokens a head sees:
+the mask form (§6, ``block_mask [B, Hkv, num_blocks]`` instead of indices)
+and the paged KV cache (§7, K/V in fixed-size physical pages reached through
+a per-sequence block table).
 """
 from __future__ import annotations
 
@@ -117,6 +122,79 @@ def decode_gqa(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_k: np.nda
             s = (kk @ q[b, hq]) / math.sqrt(D)
             p = np.exp(s - s.max())
             out[b, hq] = (p @ vv) / p.sum()
+    return out
+
+
+def _attend_one(qv: np.ndarray, kk: np.ndarray, vv: np.ndarray) -> np.ndarray:
+    """softmax(kk . qv / sqrt(D)) vv for one query vector (float64)."""
+    s = (kk @ qv) / math.sqrt(qv.shape[-1])
+    p = np.exp(s - s.max())
+    return (p @ vv) / p.sum()
+
+
+def decode_gqa_mask(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_k: np.ndarray,
+                    block_mask: np.ndarray) -> np.ndarray:
+    """Mask-form sparse GQA decode (same guide, §6: the variant whose loop
+    tests ``block_mask[b, kvh, j]`` where the index form tests
+    ``block_indices >= 0``).  Block j of sequence b is selected for KV head
+    kvh when block_mask[b, kvh, j] != 0 and j < ceil(len_b / 64); everything
+    else is as in ``decode_gqa``.
+
+    q float64 [B, Hq, D]; k, v float64 [total_k, Hkv, D]; cu_seqlens_k [B+1];
+    block_mask [B, Hkv, num_blocks] (nonzero = selected) -> float64 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        start, end = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        for hq in range(Hq):
+            kvh = hq // G
+            sel = [j for j in range(block_mask.shape[2]) if block_mask[b, kvh, j] != 0]
+            toks = decode_allowed_tokens(end - start, sel)
+            if toks.size:
+                out[b, hq] = _attend_one(q[b, hq], k[start + toks, kvh], v[start + toks, kvh])
+    return out
+
+
+def decode_gqa_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                     cache_seqlens: np.ndarray, block_table: np.ndarray,
+                     block_indices: np.ndarray) -> np.ndarray:
+    """Paged-KV sparse GQA decode (same guide, §7).
+
+    k_cache, v_cache float64 [num_pages, page_size, Hkv, D] with page_size a
+    multiple of 64; block_table [B, max_blocks_per_seq] maps a sequence's
+    logical page to a physical page; cache_seqlens [B] are the lengths.
+    Logical 64-token block i of sequence b is rows (i % r) * 64 .. +63 of
+    physical page block_table[b, i // r], r = page_size // 64, so token t
+    sits at row t % page_size of page block_table[b, t // page_size].  An
+    index selects nothing when it is < 0, >= ceil(len_b / 64), or its table
+    entry is missing or outside [0, num_pages) (the memory-safe reading).
+    Everything else is as in ``decode_gqa``.  -> float64 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    assert Hq % Hkv == 0 and page_size % BLOCK == 0
+    G = Hq // Hkv
+    r = page_size // BLOCK
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        len_b = int(cache_seqlens[b])
+        for hq in range(Hq):
+            kvh = hq // G
+            ok = []
+            for i in block_indices[b, kvh]:
+                i = int(i)
+                if i < 0 or i // r >= block_table.shape[1]:
+                    continue
+                if 0 <= int(block_table[b, i // r]) < num_pages:
+                    ok.append(i)
+            toks = decode_allowed_tokens(len_b, ok)
+            if toks.size == 0:
+                continue
+            pages = block_table[b, toks // page_size].astype(np.int64)
+            rows = toks % page_size
+            out[b, hq] = _attend_one(q[b, hq], k_cache[pages, rows, kvh], v_cache[pages, rows, kvh])
     return out
 
 
