@@ -20,7 +20,7 @@ __all__ = [
     "bsattn_build_mask_topk", "bsattn_build_mask_threshold", "bsattn_mask_to_indices",
     "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
-    "bsattn_decode_gqa", "EXPORTED_SYMBOLS",
+    "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "EXPORTED_SYMBOLS",
 ]
 
 BLOCK = 64
@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "bsattn_build_mask_threshold", "bsattn_mask_to_indices", "bsattn_fwd_workspace_bytes",
     "bsattn_fwd", "bsattn_fwd_indices", "bsattn_decode_num_splits",
     "bsattn_decode_workspace_bytes", "bsattn_decode_gqa", "bsattn_decode_default_splits",
+    "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -63,6 +64,9 @@ _SIGS = {
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "bsattn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_decode_gqa_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_decode_gqa_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                     _P, _P, _Z, _P]),
 }
 
 
@@ -238,26 +242,12 @@ def bsattn_decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> i
     return int(load_library().bsattn_decode_workspace_bytes(B, Hq, D, num_splits))
 
 
-def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0, out=None,
-                      workspace=None, stream=None):
-    """Split-KV sparse GQA decode (guide §6).  q bf16 [B,Hq,D]; k,v bf16 [total_k,Hkv,D];
-    cu_seqlens_k int32 [B+1]; block_indices int32 [B,Hkv,max_sel] (-1 = empty)."""
+def _decode_common(q, Hkv, slots, num_splits, out, workspace):
     torch = _torch()
-    _dev(q, "q", torch.bfloat16, 3)
-    _dev(k, "k", torch.bfloat16, 3)
-    _dev(v, "v", torch.bfloat16, 3)
-    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
-    _dev(block_indices, "block_indices", torch.int32, 3)
     B, Hq, D = q.shape
-    total_k, Hkv, Dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Dk != D:
-        raise ValueError("k and v must be [total_k, Hkv, D] with the query's D")
-    if cu_seqlens_k.numel() != B + 1 or block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
-        raise ValueError("cu_seqlens_k must be [B+1] and block_indices [B, Hkv, max_sel]")
-    max_sel = block_indices.shape[2]
     ns = int(num_splits)
     if ns <= 0:
-        ns = bsattn_decode_default_splits(B, Hq, Hkv, max_sel, D)
+        ns = bsattn_decode_default_splits(B, Hq, Hkv, slots, D)
         if ns <= 0:
             raise BsattnError("bsattn_decode_default_splits", 5, "could not query the device")
     if out is None:
@@ -269,7 +259,84 @@ def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0,
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    return ns, out, ws_ptr, ws_bytes
+
+
+def _decode_packed_checks(q, k, v, cu_seqlens_k):
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k, "k", torch.bfloat16, 3)
+    _dev(v, "v", torch.bfloat16, 3)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    B, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError("k and v must be [total_k, Hkv, D] with the query's D")
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_k must be [B+1]")
+    return B, Hq, Hkv, D, total_k
+
+
+def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0, out=None,
+                      workspace=None, stream=None):
+    """Split-KV sparse GQA decode (guide §6).  q bf16 [B,Hq,D]; k,v bf16 [total_k,Hkv,D];
+    cu_seqlens_k int32 [B+1]; block_indices int32 [B,Hkv,max_sel] (-1 = empty)."""
+    torch = _torch()
+    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    _dev(block_indices, "block_indices", torch.int32, 3)
+    if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
+        raise ValueError("block_indices must be [B, Hkv, max_sel]")
+    max_sel = block_indices.shape[2]
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace)
     _check("bsattn_decode_gqa", load_library().bsattn_decode_gqa(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
         max_sel, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def bsattn_decode_gqa_mask(q, k, v, cu_seqlens_k, block_mask, num_splits: int = 0, out=None,
+                           workspace=None, stream=None):
+    """Mask-form sparse GQA decode (guide §6).  As bsattn_decode_gqa, with
+    block_mask uint8/bool [B,Hkv,num_blocks] (nonzero = block selected)."""
+    torch = _torch()
+    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    _dev(block_mask, "block_mask", torch.uint8, 3)
+    if block_mask.shape[0] != B or block_mask.shape[1] != Hkv:
+        raise ValueError("block_mask must be [B, Hkv, num_blocks]")
+    nblocks = block_mask.shape[2]
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, nblocks, num_splits, out, workspace)
+    _check("bsattn_decode_gqa_mask", load_library().bsattn_decode_gqa_mask(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_mask), B, Hq, Hkv, D,
+        nblocks, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def bsattn_decode_gqa_paged(q, k_cache, v_cache, cache_seqlens, block_table, block_indices,
+                            num_splits: int = 0, out=None, workspace=None, stream=None):
+    """Paged-KV sparse GQA decode (guide §7).  q bf16 [B,Hq,D]; k_cache, v_cache bf16
+    [num_pages,page_size,Hkv,D]; cache_seqlens int32 [B]; block_table int32
+    [B,max_blocks_per_seq]; block_indices int32 [B,Hkv,max_sel] (logical 64-token blocks)."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    _dev(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    _dev(block_table, "block_table", torch.int32, 2)
+    _dev(block_indices, "block_indices", torch.int32, 3)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, Hkv, D]")
+    if cache_seqlens.numel() != B or block_table.shape[0] != B:
+        raise ValueError("cache_seqlens must be [B] and block_table [B, max_blocks_per_seq]")
+    if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
+        raise ValueError("block_indices must be [B, Hkv, max_sel]")
+    max_sel = block_indices.shape[2]
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace)
+    _check("bsattn_decode_gqa_paged", load_library().bsattn_decode_gqa_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
+        _ptr(block_indices), B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1], max_sel,
+        ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out

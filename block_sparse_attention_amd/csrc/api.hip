@@ -198,34 +198,92 @@ size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   return decode_ws(B, Hq, D, num_splits);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks and launch of the three decode forms; `a` carries the
+// form-specific pointers and sizes, `slots` is the per-(batch, KV head) slot
+// count the splits divide (max_selected_blocks, or num_blocks of a mask).
+bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!a.q || !a.k || !a.v || !a.out) return BSATTN_ERR_NULL;
+  if (a.B <= 0 || a.Hq <= 0 || a.Hkv <= 0 || slots <= 0) return BSATTN_ERR_SHAPE;
+  if (a.Hq % a.Hkv != 0) return BSATTN_ERR_SHAPE;
+  if (num_splits > slots) return BSATTN_ERR_SHAPE;
+  if (!head_dim_ok(a.D) || a.Hq / a.Hkv > 16) return BSATTN_ERR_UNSUPPORTED;
+  if (a.B > 65535 || a.Hkv > 65535) return BSATTN_ERR_SHAPE;
+  int ns = num_splits;
+  if (ns <= 0) {
+    ns = bsattn_decode_default_splits(a.B, a.Hq, a.Hkv, slots, a.D);
+    if (ns <= 0) return BSATTN_ERR_HIP;
+  }
+  const size_t need = decode_ws(a.B, a.Hq, a.D, ns);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
+  const size_t parts = (size_t)a.B * a.Hq * ns;
+  a.o_part = (float*)workspace;
+  a.lse = need ? (float*)((char*)workspace + align_up(parts * a.D * sizeof(float))) : nullptr;
+  a.max_sel = slots;
+  a.num_splits = ns;
+  return launch_decode(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
 bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* cu_seqlens_k, const int32_t* block_indices, int B,
                                 int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
                                 int num_splits, uint16_t* out, void* workspace,
                                 size_t workspace_bytes, bsattn_stream_t stream) {
-  if (!q || !k || !v || !cu_seqlens_k || !block_indices || !out) return BSATTN_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_selected_blocks <= 0 || total_k <= 0)
-    return BSATTN_ERR_SHAPE;
-  if (Hq % Hkv != 0) return BSATTN_ERR_SHAPE;
-  if (num_splits > max_selected_blocks) return BSATTN_ERR_SHAPE;
-  if (!head_dim_ok(D) || Hq / Hkv > 16) return BSATTN_ERR_UNSUPPORTED;
-  if (B > 65535 || Hkv > 65535) return BSATTN_ERR_SHAPE;
-  int ns = num_splits;
-  if (ns <= 0) {
-    ns = bsattn_decode_default_splits(B, Hq, Hkv, max_selected_blocks, D);
-    if (ns <= 0) return BSATTN_ERR_HIP;
-  }
-  const size_t need = decode_ws(B, Hq, D, ns);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
+  if (!q || !k || !v || !out || !cu_seqlens_k || !block_indices) return BSATTN_ERR_NULL;
+  if (total_k <= 0) return BSATTN_ERR_SHAPE;
   DecodeArgs a{};
-  a.q = q; a.k = k; a.v = v;
-  a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices; a.out = out;
-  const size_t parts = (size_t)B * Hq * ns;
-  a.o_part = (float*)workspace;
-  a.lse = need ? (float*)((char*)workspace + align_up(parts * D * sizeof(float))) : nullptr;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.max_sel = max_selected_blocks;
-  a.total_k = total_k; a.num_splits = ns;
-  return launch_decode(a, as_hip(stream)) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.mode = kDecodeIndices;
+  return decode_common(a, max_selected_blocks, num_splits, workspace, workspace_bytes,
+                       as_hip(stream));
+}
+
+bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* cu_seqlens_k, const uint8_t* block_mask, int B,
+                                     int Hq, int Hkv, int D, int num_blocks, int total_k,
+                                     int num_splits, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, bsattn_stream_t stream) {
+  if (!q || !k || !v || !out || !cu_seqlens_k || !block_mask) return BSATTN_ERR_NULL;
+  if (total_k <= 0) return BSATTN_ERR_SHAPE;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.cu_seqlens = cu_seqlens_k; a.block_mask = block_mask;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.mode = kDecodeMask;
+  return decode_common(a, num_blocks, num_splits, workspace, workspace_bytes, as_hip(stream));
+}
+
+bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, const int32_t* cache_seqlens,
+                                      const int32_t* block_table, const int32_t* block_indices,
+                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int max_blocks_per_seq, int max_selected_blocks,
+                                      int num_splits, uint16_t* out, void* workspace,
+                                      size_t workspace_bytes, bsattn_stream_t stream) {
+  if (!q || !k_cache || !v_cache || !out || !cache_seqlens || !block_table || !block_indices)
+    return BSATTN_ERR_NULL;
+  if (num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0) return BSATTN_ERR_SHAPE;
+  if (page_size % BSATTN_BLOCK != 0) return BSATTN_ERR_SHAPE;
+  if (!fits_elems((long double)num_pages * page_size * (Hkv > 0 ? Hkv : 1) * 128))
+    return BSATTN_ERR_SHAPE;
+  DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
+  a.cache_seqlens = cache_seqlens; a.block_table = block_table; a.block_indices = block_indices;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.num_pages = num_pages; a.page_size = page_size; a.max_blocks_per_seq = max_blocks_per_seq;
+  a.mode = kDecodePaged;
+  return decode_common(a, max_selected_blocks, num_splits, workspace, workspace_bytes,
+                       as_hip(stream));
 }
 
 }  // extern "C"

@@ -91,7 +91,13 @@ struct VTile {
   u32x4 f[DCfg<D>::kVPer];
 };
 
-template <int D>
+// A selected block: its index in the sequence, and for the paged cache its physical page.
+struct BlockRef {
+  int blk;
+  int page;
+};
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int final_out) {
   using C = DCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * C::kWaveLds];
@@ -108,11 +114,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int grp = lane >> 4;     // k-group / row group
   uint16_t* Vs = lds + w * C::kWaveLds;
 
-  // sequence extent; a malformed range is treated as empty
-  const int start = a.cu_seqlens[b];
-  const int end = a.cu_seqlens[b + 1];
-  const int len = (end >= start && end <= a.total_k && start >= 0) ? end - start : 0;
+  // sequence extent; a malformed range (or a negative paged length) is treated as empty
+  int start = 0, len = 0;
+  if constexpr (MODE == kDecodePaged) {
+    len = max(a.cache_seqlens[b], 0);
+  } else {
+    start = a.cu_seqlens[b];
+    const int end = a.cu_seqlens[b + 1];
+    len = (end >= start && end <= a.total_k && start >= 0) ? end - start : 0;
+  }
   const int nbb = (len + 63) / 64;
+  const int ratio = MODE == kDecodePaged ? a.page_size / 64 : 1;   // 64-token blocks per page
 
   // this split's slot range; this wave takes slots my_start + w + kWaves * j
   const int nslots = a.max_sel;
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const uint32_t rsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
 
-  const int32_t* idx_row = a.block_indices + ((int64_t)b * a.Hkv + kvh) * nslots;
+  const int64_t sel_row = ((int64_t)b * a.Hkv + kvh) * nslots;
 
   // Q^T as the B operand: column col = query head kvh*G + col (zero when col >= G).
   u32x4 qf[C::kSteps];
@@ -157,19 +169,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const uint32_t voff0 = (uint32_t)(lane / C::kRowChunks) * rsb + 16u * (lane % C::kRowChunks);
   const uint32_t vstep = (uint32_t)C::kTokPerInstr * rsb;
 
-  auto rsrc = [&](const uint16_t* p, int blk) {
-    const int ntok = min(64, len - blk * 64);
-    const uint16_t* base = p + ((int64_t)start + (int64_t)blk * 64) * (rsb / 2) + (int64_t)kvh * D;
+  // first row of a block: packed, row start + 64 blk; paged, row (blk % ratio) * 64 of its page
+  auto rsrc = [&](const uint16_t* p, BlockRef ref) {
+    const int ntok = min(64, len - ref.blk * 64);
+    const int64_t row = MODE == kDecodePaged
+                            ? (int64_t)ref.page * a.page_size + (int64_t)(ref.blk % ratio) * 64
+                            : (int64_t)start + (int64_t)ref.blk * 64;
+    const uint16_t* base = p + row * (rsb / 2) + (int64_t)kvh * D;
     return block_rsrc(base, (uint32_t)(ntok - 1) * rsb + D * 2);
   };
-  auto load_k = [&](int blk, KTile<D>& kt) {
+  auto load_k = [&](BlockRef blk, KTile<D>& kt) {
     const __amdgpu_buffer_rsrc_t r = rsrc(a.k, blk);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) kt.f[tt][s] = bload16(r, koff[tt], 64u * s);
   };
-  auto load_v = [&](int blk, VTile<D>& vt) {
+  auto load_v = [&](BlockRef blk, VTile<D>& vt) {
     const __amdgpu_buffer_rsrc_t r = rsrc(a.v, blk);
     // recomputed per block (not hoisted): one offset register instead of kVPer
     uint32_t vo = voff0;
@@ -180,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 
   // one selected block: S^T, softmax, O^T += V^T . P^T; with MORE, the next
   // block's K loads go out after S^T and its V loads after P.V
-  auto process = [&](int blk, int nblk, KTile<D>& kt, VTile<D>& vt, auto more_c) {
+  auto process = [&](BlockRef blk, BlockRef nblk, KTile<D>& kt, VTile<D>& vt, auto more_c) {
     constexpr bool kMore = decltype(more_c)::value;
-    const int ntok = min(64, len - blk * 64);
+    const int ntok = min(64, len - blk.blk * 64);
     // S^T tiles: token 16*tt + 4*grp + r, query column col
     f32x4 sc[4];
 #pragma unroll
@@ -261,26 +277,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   for (int c0 = 0; c0 < nper; c0 += kWave) {
     // this wave's next 64 slots: lane j holds slot my_start + w + kWaves * (c0 + j)
     int bv = -1;
-    if (c0 + lane < nper) bv = idx_row[my_start + w + kWaves * (c0 + lane)];
-    uint64_t vm = wave_ballot(bv >= 0 && bv < nbb);
+    if (c0 + lane < nper) {
+      const int slot = my_start + w + kWaves * (c0 + lane);
+      if constexpr (MODE == kDecodeMask) bv = a.block_mask[sel_row + slot] ? slot : -1;
+      else bv = a.block_indices[sel_row + slot];
+    }
+    bool ok = bv >= 0 && bv < nbb;
+    int pg = 0;
+    if constexpr (MODE == kDecodePaged) {
+      // logical page -> physical page; entries outside the table or the cache select nothing
+      const int lp = ok ? bv / ratio : 0;
+      ok = ok && lp < a.max_blocks_per_seq;
+      pg = ok ? a.block_table[(int64_t)b * a.max_blocks_per_seq + lp] : -1;
+      ok = ok && pg >= 0 && pg < a.num_pages;
+    }
+    uint64_t vm = wave_ballot(ok);
     const int n = __builtin_popcountll(vm);
     if (n == 0) continue;
     auto take = [&]() {
       const int j = __builtin_ctzll(vm);
       vm &= vm - 1;
-      return __builtin_amdgcn_readlane(bv, j);
+      return BlockRef{__builtin_amdgcn_readlane(bv, j), __builtin_amdgcn_readlane(pg, j)};
     };
     KTile<D> kt;
     VTile<D> vt;
-    int blk = take();
+    BlockRef blk = take();
     load_k(blk, kt);
     load_v(blk, vt);
     for (int i = 1; i < n; ++i) {
-      const int nblk = take();
+      const BlockRef nblk = take();
       process(blk, nblk, kt, vt, BoolC<true>{});
       blk = nblk;
     }
-    process(blk, 0, kt, vt, BoolC<false>{});
+    process(blk, BlockRef{0, 0}, kt, vt, BoolC<false>{});
   }
 
   // ---- combine the waves of this split ----
@@ -357,11 +386,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   a.out[bq * D + d] = float_to_bf16_bits(den > 0.0f ? num / den : 0.0f);
 }
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int final_out = a.num_splits == 1 ? 1 : 0;
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(a.num_splits, a.Hkv, a.B), dim3(kThreads), 0,
-                     stream, a, final_out);
+  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.num_splits, a.Hkv, a.B), dim3(kThreads),
+                     0, stream, a, final_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || final_out) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(D), 0,
@@ -369,10 +398,18 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+template <int MODE>
+hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
+  return a.D == 64 ? launch_t<64, MODE>(a, stream) : launch_t<128, MODE>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  return a.D == 64 ? launch_t<64>(a, stream) : launch_t<128>(a, stream);
+  if (a.mode == kDecodeMask) return launch_mode<kDecodeMask>(a, stream);
+  if (a.mode == kDecodePaged) return launch_mode<kDecodePaged>(a, stream);
+  return launch_mode<kDecodeIndices>(a, stream);
 }
 
 }  // namespace bsattn

@@ -30,16 +30,28 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 size_t prefill_lds_bytes(int D, int nb);
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
+// How a decode call names its keys.
+enum DecodeMode {
+  kDecodeIndices = 0,  // packed KV + cu_seqlens, block_indices [B, Hkv, max_sel]
+  kDecodeMask = 1,     // packed KV + cu_seqlens, block_mask [B, Hkv, max_sel] (slot j = block j)
+  kDecodePaged = 2,    // paged KV + cache_seqlens + block_table, block_indices
+};
+
 struct DecodeArgs {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* k;               // packed [total_k, Hkv, D] or paged [num_pages, page_size, Hkv, D]
   const uint16_t* v;
-  const int32_t* cu_seqlens;
-  const int32_t* block_indices;
+  const int32_t* cu_seqlens;       // packed modes
+  const int32_t* block_indices;    // index and paged modes
+  const uint8_t* block_mask;       // mask mode
+  const int32_t* cache_seqlens;    // paged mode
+  const int32_t* block_table;      // paged mode: [B, max_blocks_per_seq]
   uint16_t* out;
   float* o_part;   // [B, Hq, ns, D]
   float* lse;      // [B, Hq, ns]
   int B, Hq, Hkv, D, max_sel, total_k, num_splits;
+  int page_size, num_pages, max_blocks_per_seq;
+  int mode;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -29,7 +29,7 @@ import numpy as np
 
 BLOCK = 64
 
-TAG_SCORES, TAG_Q, TAG_K, TAG_V, TAG_LENS, TAG_INDICES = 0, 1, 2, 3, 4, 5
+TAG_SCORES, TAG_Q, TAG_K, TAG_V, TAG_LENS, TAG_INDICES, TAG_PAGES = 0, 1, 2, 3, 4, 5, 6
 
 
 def child_rng(seed: int, tag: int) -> np.random.Generator:
@@ -40,9 +40,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits.
 
     Inputs are finite by construction (normal / uniform draws)."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (b >> np.uint64(16)) & np.uint64(1)
-    r = (b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    # In uint32: for finite inputs (bits <= 0xFF7FFFFF) adding at most 0x8000
+    # cannot wrap.
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -192,6 +196,64 @@ def decode_inputs(cfg: DecodeConfig, seed: int = 0) -> Dict[str, np.ndarray]:
                              ("k", TAG_K, (total, cfg.Hkv, cfg.D)),
                              ("v", TAG_V, (total, cfg.Hkv, cfg.D))):
         out[name] = f32_to_bf16_bits(child_rng(seed, tag).standard_normal(shape, dtype=np.float32))
+    return out
+
+
+def decode_mask_inputs(cfg: DecodeConfig, seed: int = 0,
+                       base: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """The same workload in mask form: ``block_mask`` uint8 [B, Hkv, num_blocks]
+    with num_blocks = the longest sequence's block count; column j is 1 when
+    the index form selects block j (same draws as ``decode_inputs``, or the
+    already generated ``base``)."""
+    out = dict(base) if base is not None else decode_inputs(cfg, seed)
+    nbk = max(nblocks(int(x)) for x in out["lens"])
+    bm = np.zeros((cfg.B, cfg.Hkv, nbk), dtype=np.uint8)
+    for b in range(cfg.B):
+        for h in range(cfg.Hkv):
+            sel = out["block_indices"][b, h]
+            bm[b, h, sel[sel >= 0]] = 1
+    out["block_mask"] = bm
+    return out
+
+
+def decode_paged_inputs(cfg: DecodeConfig, seed: int = 0, page_size: int = 256,
+                        spare_pages: int = 16,
+                        base: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """The same workload with K/V scattered into a paged cache.
+
+    Sequence b's tokens fill ceil(len_b / page_size) pages taken from a seeded
+    permutation of ``num_pages`` physical pages (``spare_pages`` of them stay
+    unused and hold other draws): ``k_cache``/``v_cache`` bf16
+    [num_pages, page_size, Hkv, D], ``block_table`` int32
+    [B, max_blocks_per_seq] (-1 past a sequence's pages), ``cache_seqlens``
+    int32 [B].  Token t of sequence b is row t % page_size of page
+    block_table[b, t // page_size]; q and block_indices are those of
+    ``decode_inputs`` (or of the already generated ``base``)."""
+    out = dict(base) if base is not None else decode_inputs(cfg, seed)
+    lens = out["lens"]
+    per_seq = [-(-int(x) // page_size) for x in lens]
+    mbps = max(per_seq)
+    num_pages = sum(per_seq) + spare_pages
+    g = child_rng(seed, TAG_PAGES)
+    perm = g.permutation(num_pages)
+    kc = np.empty((num_pages, page_size, cfg.Hkv, cfg.D), dtype=np.uint16)
+    vc = np.empty_like(kc)
+    fill = f32_to_bf16_bits(g.standard_normal((2, page_size, cfg.Hkv, cfg.D), dtype=np.float32))
+    kc[:] = fill[0]
+    vc[:] = fill[1]
+    table = np.full((cfg.B, mbps), -1, dtype=np.int32)
+    cu = out["cu_seqlens_k"]
+    p = 0
+    for b in range(cfg.B):
+        for lp in range(per_seq[b]):
+            page = int(perm[p])
+            p += 1
+            table[b, lp] = page
+            t0, t1 = lp * page_size, min((lp + 1) * page_size, int(lens[b]))
+            kc[page, :t1 - t0] = out["k"][cu[b] + t0:cu[b] + t1]
+            vc[page, :t1 - t0] = out["v"][cu[b] + t0:cu[b] + t1]
+    out.update({"k_cache": kc, "v_cache": vc, "block_table": table,
+                "cache_seqlens": lens.astype(np.int32), "page_size": page_size})
     return out
 
 

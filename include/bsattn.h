@@ -183,6 +183,54 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
                                 int num_splits, uint16_t* out, void* workspace,
                                 size_t workspace_bytes, bsattn_stream_t stream);
 
+/*
+ * Mask-form sparse GQA decode (same guide, §6: the variant of the varlen
+ * decode that marks selected blocks in a boolean mask instead of listing
+ * their indices).
+ *   block_mask : uint8 [B, Hkv, num_blocks]; block j of sequence b is
+ *                selected for KV head kvh when block_mask[b, kvh, j] != 0 and
+ *                j < ceil(len_b / 64) (columns past the sequence end are
+ *                ignored).
+ * Everything else (q, k, v, cu_seqlens_k, out, the split count, workspace,
+ * GQA head mapping, the merge) is as in bsattn_decode_gqa, with num_blocks
+ * in the place of max_selected_blocks: the slots cut into num_splits ranges
+ * are the mask's columns.
+ * Errors as bsattn_decode_gqa (num_blocks <= 0 or num_splits > num_blocks:
+ * SHAPE).
+ */
+bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* cu_seqlens_k, const uint8_t* block_mask, int B,
+                                     int Hq, int Hkv, int D, int num_blocks, int total_k,
+                                     int num_splits, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, bsattn_stream_t stream);
+
+/*
+ * Paged-KV sparse GQA decode (same guide, §7: the index-form decode over a
+ * page-organised KV cache, as kept by paged-attention serving engines).
+ *   k_cache, v_cache : bfloat16 [num_pages, page_size, Hkv, D]; page_size a
+ *                      multiple of 64
+ *   cache_seqlens    : int32 [B], sequence lengths (negative: empty)
+ *   block_table      : int32 [B, max_blocks_per_seq]; logical page p of
+ *                      sequence b is physical page block_table[b, p]
+ *   block_indices    : int32 [B, Hkv, max_selected_blocks], logical 64-token
+ *                      block indices as in bsattn_decode_gqa
+ * Logical block i of sequence b is rows (i % r) * 64 .. +63 of physical page
+ * block_table[b, i / r], r = page_size / 64.  An index selects nothing when
+ * it is < 0 or >= ceil(len_b / 64), when i / r >= max_blocks_per_seq, or when
+ * its table entry is outside [0, num_pages).  q, out, split count, workspace,
+ * GQA head mapping and merge as in bsattn_decode_gqa.
+ * Errors: NULL pointers; num_pages, page_size, max_blocks_per_seq <= 0 or
+ * page_size % 64 != 0, and the shape errors of bsattn_decode_gqa (SHAPE);
+ * D / group size as bsattn_decode_gqa (UNSUPPORTED); workspace (WORKSPACE).
+ */
+bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, const int32_t* cache_seqlens,
+                                      const int32_t* block_table, const int32_t* block_indices,
+                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int max_blocks_per_seq, int max_selected_blocks,
+                                      int num_splits, uint16_t* out, void* workspace,
+                                      size_t workspace_bytes, bsattn_stream_t stream);
+
 /* The split count bsattn_decode_gqa would use for num_splits <= 0 on the
  * current device (queries the CU count once per device). Returns 0 on error. */
 int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D);

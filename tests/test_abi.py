@@ -90,6 +90,43 @@ def test_decode_validates_on_host():
     assert lib.bsattn_decode_workspace_bytes(0, 8, 128, 2) == 0
 
 
+def test_mask_form_decode_validates_on_host():
+    lib = _lib()
+    F = FAKE
+
+    def call(q=F, bm=F, B=2, Hq=8, Hkv=2, D=128, nbk=4, tk=100, ns=2, ws=None, wsb=0):
+        return lib.bsattn_decode_gqa_mask(q, F, F, F, bm, B, Hq, Hkv, D, nbk, tk, ns, F, ws, wsb, None)
+
+    assert call(q=None) == 1
+    assert call(bm=None) == 1
+    assert call(nbk=0) == 2
+    assert call(ns=5) == 2                 # more splits than mask columns
+    assert call(tk=0) == 2
+    assert call(Hq=6, Hkv=4) == 2
+    assert call(D=96) == 3
+    assert call(ns=2) == 4
+
+
+def test_paged_decode_validates_on_host():
+    lib = _lib()
+    F = FAKE
+
+    def call(q=F, tab=F, B=2, Hq=8, Hkv=2, D=128, npg=16, psz=256, mbps=4, ms=8, ns=2, ws=None, wsb=0):
+        return lib.bsattn_decode_gqa_paged(q, F, F, F, tab, F, B, Hq, Hkv, D, npg, psz, mbps, ms, ns,
+                                           F, ws, wsb, None)
+
+    assert call(q=None) == 1
+    assert call(tab=None) == 1
+    assert call(psz=96) == 2               # page size not a multiple of 64
+    assert call(psz=0) == 2
+    assert call(npg=0) == 2
+    assert call(mbps=0) == 2
+    assert call(ms=0) == 2
+    assert call(ns=9) == 2
+    assert call(Hq=34, Hkv=2) == 3
+    assert call(ns=2) == 4
+
+
 def test_library_heuristic_matches_oracle_sweep():
     _lib()
     n = 0
