@@ -59,23 +59,34 @@ def _softmax_rows(s: np.ndarray, allowed: np.ndarray, v: np.ndarray) -> np.ndarr
 
 def prefill_head_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.ndarray,
                       is_causal: bool, rows: Optional[Sequence[int]] = None) -> np.ndarray:
-    """One (batch, head): q, k, v float64 [S, D]; block_mask [nb, nb].
+    """One (batch, head): q float64 [Sq, D]; k, v float64 [Sk, D] with Sk >= Sq;
+    block_mask [ceil(Sq/64), ceil(Sk/64)].
 
-    Returns float64 [len(rows), D] (all S rows when ``rows`` is None)."""
-    S, D = q.shape
-    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
-    t = np.arange(S)
+    With Sk > Sq the queries are the last Sq positions of an Sk-token context
+    (past = Sk - Sq, as the TileLang FlashAttention guide's BHSD example
+    aligns the causal mask with ``q_idx = row + past_len``, and the
+    block-sparse guide's §8 Triton reference with PAST_LEN): query row r sees
+    key t when its block is selected, t < Sk, and, if causal, t <= r + past.
+
+    Returns float64 [len(rows), D] (all Sq rows when ``rows`` is None)."""
+    Sq, D = q.shape
+    Sk = k.shape[0]
+    past = Sk - Sq
+    assert past >= 0
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    t = np.arange(Sk)
     kb = t // BLOCK
     s = (q[rows] @ k.T) / math.sqrt(D)
     allowed = block_mask[rows // BLOCK][:, kb] != 0
     if is_causal:
-        allowed &= t[None, :] <= rows[:, None]
+        allowed &= t[None, :] <= rows[:, None] + past
     return _softmax_rows(s, allowed, v)
 
 
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.ndarray,
             is_causal: bool, row_chunk: int = 256) -> np.ndarray:
-    """q, k, v float64 [B, H, S, D]; block_mask [B, H, nb, nb] -> float64 [B, H, S, D].
+    """q float64 [B, H, Sq, D]; k, v float64 [B, H, Sk, D] (Sk >= Sq, usually
+    equal); block_mask [B, H, ceil(Sq/64), ceil(Sk/64)] -> float64 [B, H, Sq, D].
 
     Rows are independent, so they are evaluated a chunk at a time only to
     bound memory."""
