@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 __all__ = [
     "BLOCK", "BsattnError", "load_library", "bsattn_status_string", "bsattn_version",
     "bsattn_build_mask_topk", "bsattn_build_mask_threshold", "bsattn_mask_to_indices",
-    "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices",
+    "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices", "bsattn_fwd_chunk",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
     "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "EXPORTED_SYMBOLS",
 ]
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "bsattn_build_mask_threshold", "bsattn_mask_to_indices", "bsattn_fwd_workspace_bytes",
     "bsattn_fwd", "bsattn_fwd_indices", "bsattn_decode_num_splits",
     "bsattn_decode_workspace_bytes", "bsattn_decode_gqa", "bsattn_decode_default_splits",
-    "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
+    "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "bsattn_fwd_chunk",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -60,6 +60,7 @@ _SIGS = {
     "bsattn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "bsattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_fwd_indices": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_fwd_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "bsattn_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -225,6 +226,32 @@ def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stre
     _dev(out, "out", torch.bfloat16, 4)
     _check("bsattn_fwd_indices", load_library().bsattn_fwd_indices(
         _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), B, H, S, D, int(bool(is_causal)),
+        _ptr(out), _stream(stream)))
+    return out
+
+
+def bsattn_fwd_chunk(q, k, v, block_mask, is_causal: bool = True, out=None, stream=None):
+    """Forward pass for Sq queries at the end of an Sk-token context (Sq <= Sk):
+    q bf16 [B,H,Sq,D]; k, v bf16 [B,H,Sk,D]; block_mask uint8/bool
+    [B,H,ceil(Sq/64),ceil(Sk/64)].  Causal rows see keys t <= row + Sk - Sq."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(k, "k", torch.bfloat16, 4)
+    _dev(v, "v", torch.bfloat16, 4)
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    Sk = k.shape[2]
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    _dev(block_mask, "block_mask", torch.uint8, 4)
+    if tuple(block_mask.shape) != (B, H, -(-Sq // BLOCK), -(-Sk // BLOCK)):
+        raise ValueError("block_mask must be [B, H, ceil(Sq/64), ceil(Sk/64)]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, 4)
+    _check("bsattn_fwd_chunk", load_library().bsattn_fwd_chunk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), B, H, Sq, Sk, D, int(bool(is_causal)),
         _ptr(out), _stream(stream)))
     return out
 

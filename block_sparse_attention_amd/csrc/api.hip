@@ -140,19 +140,20 @@ size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
 
 static bsattn_status fwd_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint8_t* mask, const int32_t* idx, const int32_t* cnt,
-                                int B, int H, int S, int D, int is_causal, uint16_t* out,
+                                int B, int H, int Sq, int Sk, int D, int is_causal, uint16_t* out,
                                 hipStream_t stream) {
-  if (B <= 0 || H <= 0 || S <= 0) return BSATTN_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
-  if ((long long)B * H * nblocks(S) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if ((long long)B * H * nblocks(Sq) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   // block lists are held as 16-bit entries in LDS next to the K/V ring
-  if (nblocks(S) > 65535 || prefill_lds_bytes(D, nblocks(S)) > kMaxLdsBytes)
+  if (nblocks(Sk) > 65535 || prefill_lds_bytes(D, nblocks(Sk)) > kMaxLdsBytes)
     return BSATTN_ERR_UNSUPPORTED;
-  if (!fits_elems((long double)B * H * S * D)) return BSATTN_ERR_SHAPE;
+  if (!fits_elems((long double)B * H * Sk * D)) return BSATTN_ERR_SHAPE;
   PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.mask = mask; a.idx = idx; a.cnt = cnt;
-  a.B = B; a.H = H; a.S = S; a.D = D; a.nb = nblocks(S);
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
+  a.nbq = nblocks(Sq); a.nbk = nblocks(Sk);
   a.causal = is_causal ? 1 : 0;
   return launch_prefill(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
@@ -166,7 +167,15 @@ bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
     const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
     if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
   }
-  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, S, D, is_causal, out,
+  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, S, S, D, is_causal, out,
+                    as_hip(stream));
+}
+
+bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint8_t* block_mask, int B, int H, int Sq, int Sk, int D,
+                               int is_causal, uint16_t* out, bsattn_stream_t stream) {
+  if (!q || !k || !v || !block_mask || !out) return BSATTN_ERR_NULL;
+  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, Sq, Sk, D, is_causal, out,
                     as_hip(stream));
 }
 
@@ -174,7 +183,7 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
                                  const int32_t* idx, const int32_t* cnt, int B, int H, int S,
                                  int D, int is_causal, uint16_t* out, bsattn_stream_t stream) {
   if (!q || !k || !v || !idx || !cnt || !out) return BSATTN_ERR_NULL;
-  return fwd_common(q, k, v, nullptr, idx, cnt, B, H, S, D, is_causal, out, as_hip(stream));
+  return fwd_common(q, k, v, nullptr, idx, cnt, B, H, S, S, D, is_causal, out, as_hip(stream));
 }
 
 int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,

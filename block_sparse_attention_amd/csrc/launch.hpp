@@ -15,19 +15,19 @@ hipError_t launch_compact(const uint8_t* mask, int B, int H, int nb, int causal,
                           int32_t* cnt, hipStream_t stream);
 
 struct PrefillArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* out;
-  const uint8_t* mask;   // [B,H,nb,nb] mask form, or nullptr
-  const int32_t* idx;    // [B,H,nb,nb] list form, or nullptr
-  const int32_t* cnt;    // [B,H,nb]
-  int B, H, S, D, nb;
+  const uint16_t* q;     // [B,H,Sq,D]
+  const uint16_t* k;     // [B,H,Sk,D]
+  const uint16_t* v;     // [B,H,Sk,D]
+  uint16_t* out;         // [B,H,Sq,D]
+  const uint8_t* mask;   // [B,H,nbq,nbk] mask form, or nullptr
+  const int32_t* idx;    // [B,H,nbq,nbk] list form, or nullptr
+  const int32_t* cnt;    // [B,H,nbq]
+  int B, H, Sq, Sk, D, nbq, nbk;   // Sq <= Sk: the queries are the last Sq positions
   int causal;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// LDS one forward work-group needs (K/V ring plus the block list).
-size_t prefill_lds_bytes(int D, int nb);
+// LDS one forward work-group needs (K/V ring plus a block list of nbk entries).
+size_t prefill_lds_bytes(int D, int nbk);
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 // How a decode call names its keys.

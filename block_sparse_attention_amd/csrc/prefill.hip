@@ -24,9 +24,14 @@
 // * Software pipeline over the active blocks t = 0, 1, ...: while the VALU
 //   works on the softmax of block t, the matrix cores run P.V of block t-1
 //   and Q.K^T of block t+1.
-// * The mask row is compacted once, at the start, into a list of key blocks
-//   in LDS (64-column ballots); the one block that needs in-block masking
-//   (the causal diagonal or the ragged tail) is put last.
+// * The mask row is compacted once, at the start, into the ascending list of
+//   key blocks in LDS (64-column ballots); a block whose keys are not all
+//   visible to every row (on the causal diagonal, or past the end of K) is
+//   masked when its scores come up.
+// * Queries may be fewer than keys (Sq <= Sk): they are then the last Sq
+//   positions, and the causal rule compares key t with row + Sk - Sq (the
+//   TileLang FlashAttention guide's BHSD example, past_len; the block-sparse
+//   guide's §8 Triton reference, PAST_LEN).
 // * K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no
 //   registers) into two-slot rings, one block ahead, with explicit vmcnt
 //   waits.  Rows are XOR-swizzled in 16-byte granules so the K reads
@@ -191,70 +196,66 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   const int h = lane >> 5;   // which half of the key rows / k-group this lane holds
   const int n = lane & 31;   // query row within the wave's 32
 
-  const int nb = a.nb;
-  const int S = a.S;
+  const int nbq = a.nbq, nbk = a.nbk;
+  const int Sq = a.Sq, Sk = a.Sk;
+  const int past = Sk - Sq;   // query row r sits at key position r + past
   int bh, i;
-  map_item(blockIdx.x, a.B * a.H, nb, map_mode, group, bh, i);
+  map_item(blockIdx.x, a.B * a.H, nbq, map_mode, group, bh, i);
 
-  const int64_t head_off = (int64_t)bh * S * D;
-  const uint16_t* __restrict__ Q = a.q + head_off;
-  const uint16_t* __restrict__ K = a.k + head_off;
-  const uint16_t* __restrict__ V = a.v + head_off;
+  const int64_t q_off = (int64_t)bh * Sq * D;
+  const int64_t kv_off = (int64_t)bh * Sk * D;
+  const uint16_t* __restrict__ Q = a.q + q_off;
+  const uint16_t* __restrict__ K = a.k + kv_off;
+  const uint16_t* __restrict__ V = a.v + kv_off;
   const int q0 = i * 64;
   const int qrow = q0 + 32 * rg + n;
-  const int lim = CAUSAL ? min(i + 1, nb) : nb;
-  // The one key block that needs masking inside the block: the causal
-  // diagonal, or without causality the ragged last block; -1 for none.
-  const int special = CAUSAL ? i : ((S % 64) ? nb - 1 : -1);
+  // Key blocks past the last one any row of this query block can see are skipped.
+  const int lim = CAUSAL ? min(nbk, ((q0 + 63 + past) >> 6) + 1) : nbk;
+  // A key block needs masking inside the block when some of its keys lie
+  // after the first query row's position (causal), or past the end of K.
+  auto needs_mask = [&](int j) {
+    return (CAUSAL && j * 64 + 63 > q0 + past) || (j * 64 + 64 > Sk);
+  };
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds row qrow, dims 16s + 8h .. +8.
   u32x4 qf[C::kSteps];
   {
-    const int qr = min(qrow, S - 1);   // rows past the end are never stored
+    const int qr = min(qrow, Sq - 1);   // rows past the end are never stored
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
       qf[s] = *(const u32x4*)(Q + (int64_t)qr * D + 16 * s + 8 * h);
   }
 
   // ---- compact this query block's mask row (or list) into LDS ----
-  // Unmasked blocks first, in the order found; the special block last.
   if (w == 0) {
     int count = 0;
-    bool has_special = false;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     if constexpr (LIST) {
-      const int64_t row = (int64_t)bh * nb + i;
-      const int nl = max(0, min(a.cnt[row], nb));
-      const int32_t* src = a.idx + row * nb;
+      const int64_t row = (int64_t)bh * nbq + i;
+      const int nl = max(0, min(a.cnt[row], nbk));
+      const int32_t* src = a.idx + row * nbk;
       for (int c0 = 0; c0 < nl; c0 += kWave) {
         const int p = c0 + lane;
         const int j = p < nl ? src[p] : -1;
-        const bool sel = j >= 0 && j < lim;
-        const bool ok = sel && j != special;
+        const bool ok = j >= 0 && j < lim;
         const uint64_t bits = wave_ballot(ok);
         if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
         count += __popcll(bits);
-        has_special |= wave_ballot(sel && j == special) != 0;
       }
     } else {
-      const uint8_t* mrow = a.mask + ((int64_t)bh * nb + i) * nb;
+      const uint8_t* mrow = a.mask + ((int64_t)bh * nbq + i) * nbk;
       for (int c0 = 0; c0 < lim; c0 += kWave) {
         const int j = c0 + lane;
-        const bool sel = j < lim && mrow[j] != 0;
-        const bool ok = sel && j != special;
+        const bool ok = j < lim && mrow[j] != 0;
         const uint64_t bits = wave_ballot(ok);
         if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
         count += __popcll(bits);
-        has_special |= wave_ballot(sel && j == special) != 0;
       }
     }
-    if (lane == 0) {
-      if (has_special) list[count++] = (uint16_t)special;
-      list[nb] = (uint16_t)count;   // the slot after the list holds its length
-    }
+    if (lane == 0) list[nbk] = (uint16_t)count;   // the slot after the list holds its length
   }
   __syncthreads();
-  const int nblk = __builtin_amdgcn_readfirstlane((int)list[nb]);
+  const int nblk = __builtin_amdgcn_readfirstlane((int)list[nbk]);
 
   // ---- per-lane DMA source byte offsets for this wave's share of a tile ----
   // Instruction kk covers tile rows kk*kRowsPerInstr .. +kRowsPerInstr-1; lane l
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     constexpr bool kV = decltype(is_v)::value;
     const int j = __builtin_amdgcn_readfirstlane(jv);
     const uint16_t* base = (kV ? V : K) + (int64_t)j * 64 * D;
-    const int last = S - 1 - j * 64;
+    const int last = Sk - 1 - j * 64;
     if (last >= 63) {
 #pragma unroll
       for (int q = 0; q < C::kWaveInstr; ++q)
@@ -321,7 +322,9 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   f32x16 o[C::kDT];
 #pragma unroll
   for (int t = 0; t < C::kDT; ++t) o[t] = f32x16{};
-  float m = -INFINITY;
+  // m: the exponent offset in use for this lane's row (always finite; 0 until
+  // a block shows the row a finite score); l: the running row sum.
+  float m = 0.0f;
   float l = 0.0f;
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
 
@@ -351,12 +354,12 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       }
     }
   };
-  // In-block masking of key block j: keys past the end, and keys after the
-  // query row on the causal diagonal, get -inf.
+  // In-block masking of key block j: keys past the end of K, and (causal)
+  // keys after the query row's position, get -inf.
   auto mask_block = [&](int j, Sc& sc) {
     const int kbase = j * 64 + 32 * NT * kh;
-    int vis = S - kbase;
-    if (CAUSAL && j == i) vis = min(vis, qrow - kbase + 1);
+    int vis = Sk - kbase;
+    if (CAUSAL) vis = min(vis, qrow + past - kbase + 1);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -407,25 +410,25 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   };
   // Raise m to the block's row maxima, rescale o and l, redo the exponentials.
   auto raise = [&](const Sc& sc, Pr& pr) -> float {
-    const float m_new = fmaxf(m, row_max(sc));
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);
+    const float m_new = fmaxf(m, row_max(sc));   // a fully masked row keeps its m
+    const float alpha = fast_exp2((m - m_new) * c);
     l *= alpha;
 #pragma unroll
     for (int tt = 0; tt < C::kDT; ++tt)
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) o[tt][ii] *= alpha;
     m = m_new;
-    return exps(sc, pr, m_use * c);
+    return exps(sc, pr, m * c);
   };
-  // First block of an item: m = row max.
+  // First block of an item: m = row max (0 for a row it fully masks).
   auto softmax_first = [&](const Sc& sc, Pr& pr) {
-    m = row_max(sc);
-    l = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
+    const float mx = row_max(sc);
+    m = (mx == -INFINITY) ? 0.0f : mx;
+    l = exps(sc, pr, m * c);
   };
   // Any later block, outside the pipelined loop.
   auto softmax = [&](const Sc& sc, Pr& pr) {
-    float rs = exps(sc, pr, (m == -INFINITY) ? 0.0f : m * c);
+    float rs = exps(sc, pr, m * c);
     // keep the first pass ahead of the redo test
 #pragma unroll
     for (int u = 0; u < 2 * NT; ++u) asm volatile("" ::"v"(pr.p[u]));
@@ -472,10 +475,12 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
                     const Pr& p_prev, Pr& p_cur) {
     constexpr uint32_t kN = decltype(kn)::value;
     constexpr uint32_t kVP = decltype(vp)::value;
+    const int jt = __builtin_amdgcn_readfirstlane((int)list[t]);
     wait_vmem<0>();
     barrier_raw();
-    issue(vt, IsV{}, list[t]);
+    issue(vt, IsV{}, jt);
     if (t + 2 < nblk) issue(kt, IsK{}, list[t + 2]);
+    if (needs_mask(jt)) mask_block(jt, s_cur);
 
     u32x4 op[kSlots];
     auto read = [&](auto k_c) {
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         s_next.s[tile] = mfma32(op[k], qf[st], st == 0 ? f32x16{} : s_next.s[tile]);
       }
     };
-    const float mc = (m == -INFINITY) ? 0.0f : m * c;
+    const float mc = m * c;
     float rs = 0.0f;
     float pe[16 * NT];
     auto valu = [&](auto k_c) {
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     barrier_raw();
     issue(vt, IsV{}, list[t]);
     pv(vp, p_prev);
-    if (j == special) mask_block(j, s_cur);
+    if (needs_mask(j)) mask_block(j, s_cur);
     softmax(s_cur, p_cur);
     wait_vmem<0>();
     barrier_raw();
@@ -551,6 +556,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     barrier_raw();
     if (2 < nblk) issue(K0{}, IsK{}, list[2]);
     qk(K1{}, sb);
+    const int j0 = __builtin_amdgcn_readfirstlane((int)list[0]);
+    if (needs_mask(j0)) mask_block(j0, sa);
     softmax_first(sa, pa);
     int t = 1;
     for (; t + 2 <= nblk - 1; t += 2) {
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     else last(V0{}, V1{}, t, sa, pb, pa);
   } else if (nblk == 1) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[0]);
-    if (j == special) mask_block(j, sa);
+    if (needs_mask(j)) mask_block(j, sa);
     softmax_first(sa, pa);
     wait_vmem<0>();
     barrier_raw();
@@ -583,8 +590,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     // one wave holds the whole row: normalise and store
     const float lt = sum_with_half_swap(l);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (qrow < S) {
-      uint16_t* __restrict__ O = a.out + head_off + (int64_t)qrow * D;
+    if (qrow < Sq) {
+      uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
@@ -615,15 +622,15 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   const float m_b = stats[pw * 2 * kWave + lane];
   const float l_b = stats[pw * 2 * kWave + kWave + lane];
   const float l_a = sum_with_half_swap(l);
-  const float M = fmaxf(m, m_b);
-  const float al_a = (m == -INFINITY) ? 0.0f : fast_exp2((m - M) * c);
-  const float al_b = (m_b == -INFINITY) ? 0.0f : fast_exp2((m_b - M) * c);
+  const float M = fmaxf(m, m_b);   // both finite
+  const float al_a = fast_exp2((m - M) * c);
+  const float al_b = fast_exp2((m_b - M) * c);
   const float lt = l_a * al_a + l_b * al_b;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const float fa = al_a * inv, fb = al_b * inv;
   auto finish = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
-    uint16_t* __restrict__ O = a.out + head_off + (int64_t)qrow * D;
+    uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
 #pragma unroll
     for (int t = 0; t < kHalf; ++t) {
       constexpr int kBase = KH * kHalf;
@@ -640,7 +647,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       }
     }
   };
-  if (qrow < S) {
+  if (qrow < Sq) {
     if (kh == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
   }
@@ -667,20 +674,20 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   if (BH % 8 == 0) {
     mode = 1;
     const int per_xcd = BH / 8;
-    const double kv_bytes = 2.0 * a.S * D * 2.0;
+    const double kv_bytes = 2.0 * a.Sk * D * 2.0;
     int g = (int)(4.0 * 1024 * 1024 / kv_bytes);
     g = max(1, min(g, per_xcd));
     while (per_xcd % g) --g;
     group = g;
   }
-  const size_t lds = lds_bytes<D, KS>(a.nb);
+  const size_t lds = lds_bytes<D, KS>(a.nbk);
   auto kern = prefill_kernel<D, KS, CAUSAL, LIST>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int64_t items = (int64_t)BH * a.nb;
+  const int64_t items = (int64_t)BH * a.nbq;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
                      group);
   return hipGetLastError();
@@ -688,8 +695,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t prefill_lds_bytes(int D, int nb) {
-  return D == 64 ? lds_bytes<64, kKeySplits<64>>(nb) : lds_bytes<128, kKeySplits<128>>(nb);
+size_t prefill_lds_bytes(int D, int nbk) {
+  return D == 64 ? lds_bytes<64, kKeySplits<64>>(nbk) : lds_bytes<128, kKeySplits<128>>(nbk);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

@@ -131,6 +131,23 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
                                  const int32_t* idx, const int32_t* cnt, int B, int H, int S,
                                  int D, int is_causal, uint16_t* out, bsattn_stream_t stream);
 
+/*
+ * Forward pass for a chunk of queries at the end of a longer context
+ * (chunked or incremental prefill): q and out bfloat16 [B, H, Sq, D], k and
+ * v bfloat16 [B, H, Sk, D] with Sq <= Sk, block_mask uint8
+ * [B, H, ceil(Sq/64), ceil(Sk/64)] (nonzero = selected).  Query row r is
+ * position r + (Sk - Sq) of the context: with is_causal it sees key t only
+ * when t <= r + Sk - Sq (the TileLang FlashAttention guide's BHSD example,
+ * past_len = seq_kv - seq_q; the block-sparse guide's §8 Triton reference,
+ * PAST_LEN).  Keys at or past Sk are masked; rows with no visible key output
+ * 0.  Sq = Sk is bsattn_fwd.  Needs no workspace.
+ * Errors: NULL pointers; B, H, Sq <= 0 or Sk < Sq (SHAPE); D not 64 or 128,
+ * or ceil(Sk/64) too large for the on-chip block list (UNSUPPORTED).
+ */
+bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint8_t* block_mask, int B, int H, int Sq, int Sk, int D,
+                               int is_causal, uint16_t* out, bsattn_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sparse GQA decode                                                         */
 /* ------------------------------------------------------------------------ */

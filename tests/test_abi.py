@@ -90,6 +90,17 @@ def test_decode_validates_on_host():
     assert lib.bsattn_decode_workspace_bytes(0, 8, 128, 2) == 0
 
 
+def test_chunk_fwd_validates_on_host():
+    lib = _lib()
+    F = FAKE
+    assert lib.bsattn_fwd_chunk(None, F, F, F, 1, 1, 64, 128, 64, 1, F, None) == 1
+    assert lib.bsattn_fwd_chunk(F, F, F, None, 1, 1, 64, 128, 64, 1, F, None) == 1
+    assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 129, 128, 64, 1, F, None) == 2   # Sq > Sk
+    assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 0, 128, 64, 1, F, None) == 2
+    assert lib.bsattn_fwd_chunk(F, F, F, F, 0, 1, 64, 128, 64, 1, F, None) == 2
+    assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 64, 128, 96, 1, F, None) == 3
+
+
 def test_mask_form_decode_validates_on_host():
     lib = _lib()
     F = FAKE

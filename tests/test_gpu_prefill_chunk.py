@@ -1,0 +1,91 @@
+"""GPU parity: prefill with fewer queries than keys (Sq <= Sk) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_amd as bsa
+from block_sparse_attention_amd import inputs as gen
+from oracle import attention as oa
+from oracle import mask as om
+from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, H, Sq, Sk, D, seed, density=0.4):
+    rng = np.random.default_rng(seed)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sq, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sk, D), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sk, D), dtype=np.float32))
+    nbq, nbk = -(-Sq // 64), -(-Sk // 64)
+    m = (rng.random((B, H, nbq, nbk)) < density).astype(np.uint8)
+    return q, k, v, m
+
+
+def _gpu(q, k, v, m, causal):
+    return gpu_bf16_to_f64(bsa.bsattn_fwd_chunk(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
+                                                to_gpu(m), causal))
+
+
+def _oracle(q, k, v, m, causal):
+    f = gen.bf16_bits_to_f64
+    return oa.prefill(f(q), f(k), f(v), m, causal)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sq,Sk", [(64, 256), (128, 448), (100, 300), (1, 130), (200, 201),
+                                   (65, 4000), (256, 256)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_every_element(Sq, Sk, D, causal):
+    q, k, v, m = _case(2, 3, Sq, Sk, D, Sq * 31 + Sk + D)
+    say(f"[prefill-chunk] Sq={Sq} Sk={Sk} D={D} causal={causal} blocks={int(m.sum())}")
+    check_close(_gpu(q, k, v, m, causal), _oracle(q, k, v, m, causal),
+                f"chunk Sq{Sq} Sk{Sk} D{D} c{causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_chunk_dense_and_empty_rows(D):
+    # dense mask: every causal key; empty mask rows: output 0
+    q, k, v, _ = _case(1, 2, 192, 700, D, 5 + D)
+    nbq, nbk = 3, 11
+    m = np.ones((1, 2, nbq, nbk), np.uint8)
+    m[0, 1, 1, :] = 0
+    say(f"[prefill-chunk] dense + empty row D={D}")
+    got = _gpu(q, k, v, m, True)
+    check_close(got, _oracle(q, k, v, m, True), f"chunk dense D{D}")
+    assert (got[0, 1, 64:128] == 0).all()
+
+
+def test_square_chunk_is_the_square_forward_bitwise():
+    cfg = gen.CONFIGS["C1"]
+    inp = gen.prefill_inputs(cfg, 0)
+    m = om.build_mask_topk(inp["scores"], cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
+    q, k, v = (to_gpu_bf16(inp[n]) for n in ("q", "k", "v"))
+    a = bsa.bsattn_fwd(q, k, v, to_gpu(m), True)
+    b = bsa.bsattn_fwd_chunk(q, k, v, to_gpu(m), True)
+    say("[prefill-chunk] Sq = Sk vs bsattn_fwd")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_chunk_large_sampled_rows():
+    """A 2048-query chunk at the end of a 16384-token context, D 128, top-k
+    mask rows: sampled rows against the oracle computed row by row."""
+    B, H, Sq, Sk, D = 1, 8, 2048, 16384, 128
+    rng = np.random.default_rng(77)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sq, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sk, D), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, H, Sk, D), dtype=np.float32))
+    nbq, nbk = Sq // 64, Sk // 64
+    scores = rng.standard_normal((B, H, nbq, nbk), dtype=np.float32)
+    top = np.argsort(-scores, axis=-1, kind="stable")[..., :24]
+    m = np.zeros((B, H, nbq, nbk), np.uint8)
+    np.put_along_axis(m, top, 1, axis=-1)
+    past_blocks = (Sk - Sq) // 64
+    m[..., np.arange(nbq), past_blocks + np.arange(nbq)] = 1   # each row's diagonal block
+    say(f"[prefill-chunk] large Sq={Sq} Sk={Sk} blocks={int(m.sum())}")
+    got = _gpu(q, k, v, m, True)
+    f = gen.bf16_bits_to_f64
+    rows = sorted({0, 1, 63, 64, 65, 1023, 2047} | set(rng.integers(0, Sq, 5).tolist()))
+    for h in (0, 5):
+        want = oa.prefill_head_rows(f(q[0, h]), f(k[0, h]), f(v[0, h]), m[0, h], True, rows)
+        check_close(got[0, h, rows], want, f"large chunk h{h}")
