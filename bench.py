@@ -17,6 +17,9 @@ Printed (one JSON line):
                256 MiB last-level cache flushed before every timed call by
                reading a 512 MiB buffer (a read leaves no dirty lines whose
                write-back would land inside the timed call);
+* next_rows  — the mask-form and paged-KV variants of that decode (same
+               workload and flush) and a chunked prefill (the last 1024 of
+               C2's 4096 positions), each against the same roofline;
 * cpu_baseline — the float64 CPU oracle timed on a bounded sample of the same
                workload on this host.
 
@@ -25,6 +28,7 @@ Inputs are synthetic (seeded generator) and resident in HBM before timing.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -144,57 +148,129 @@ def bench_prefill(cfg_name: str, steps: int, warmup: int):
     }
 
 
-def bench_decode(steps: int, warmup: int):
-    torch = _torch()
-    import block_sparse_attention_amd as bsa
-    from block_sparse_attention_amd import inputs as gen
-
-    cfg = gen.CONFIGS["C5"]
-    d = gen.decode_inputs(cfg, 0)
-    q, k, v = (_gpu_bf16(d[n]) for n in ("q", "k", "v"))
-    cu = torch.from_numpy(d["cu_seqlens_k"]).to("cuda")
-    idx = torch.from_numpy(d["block_indices"]).to("cuda")
-    ns = bsa.bsattn_decode_default_splits(cfg.B, cfg.Hq, cfg.Hkv, cfg.max_selected_blocks, cfg.D)
-    out = torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=torch.bfloat16, device="cuda")
-    ws_bytes = bsa.bsattn_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.D, ns)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-
-    # algorithmic bytes: selected K and V tokens, q, out, block lists, cu_seqlens
+def _selected_tokens(d, cfg):
     lens = d["lens"]
-    sel_tokens = 0
+    sel = 0
     for b in range(cfg.B):
         nbb = -(-int(lens[b]) // 64)
         for h in range(cfg.Hkv):
             for i in d["block_indices"][b, h]:
                 if 0 <= i < nbb:
-                    sel_tokens += min(64, int(lens[b]) - 64 * int(i))
-    algo_bytes = (sel_tokens * 2 * cfg.D * 2 + q.numel() * 2 + out.numel() * 2
-                  + idx.numel() * 4 + cu.numel() * 4)
+                    sel += min(64, int(lens[b]) - 64 * int(i))
+    return sel
+
+
+def bench_decode(steps: int, warmup: int, form: str = "indices", base=None, page_size: int = 256):
+    """Per-call time of one sparse GQA decode call on C5, in the index form
+    (packed KV), the mask form, or over a paged KV cache (pages of page_size)."""
+    torch = _torch()
+    import block_sparse_attention_amd as bsa
+    from block_sparse_attention_amd import inputs as gen
+
+    cfg = gen.CONFIGS["C5"]
+    d = base if base is not None else gen.decode_inputs(cfg, 0)
+    q = _gpu_bf16(d["q"])
+    out = torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=torch.bfloat16, device="cuda")
+    sel_tokens = _selected_tokens(d, cfg)
+    meta = 0
+    if form == "indices":
+        k, v = _gpu_bf16(d["k"]), _gpu_bf16(d["v"])
+        cu = torch.from_numpy(d["cu_seqlens_k"]).to("cuda")
+        idx = torch.from_numpy(d["block_indices"]).to("cuda")
+        slots = idx.shape[2]
+        meta = idx.numel() * 4 + cu.numel() * 4
+        call_args = lambda ns, ws: bsa.bsattn_decode_gqa(q, k, v, cu, idx, num_splits=ns, out=out, workspace=ws)
+    elif form == "mask":
+        dm = gen.decode_mask_inputs(cfg, 0, base=d)
+        k, v = _gpu_bf16(d["k"]), _gpu_bf16(d["v"])
+        cu = torch.from_numpy(d["cu_seqlens_k"]).to("cuda")
+        bm = torch.from_numpy(dm["block_mask"]).to("cuda")
+        slots = bm.shape[2]
+        meta = bm.numel() + cu.numel() * 4
+        call_args = lambda ns, ws: bsa.bsattn_decode_gqa_mask(q, k, v, cu, bm, num_splits=ns, out=out, workspace=ws)
+    else:
+        dp = gen.decode_paged_inputs(cfg, 0, page_size=page_size, base=d)
+        k, v = _gpu_bf16(dp["k_cache"]), _gpu_bf16(dp["v_cache"])
+        sl = torch.from_numpy(dp["cache_seqlens"]).to("cuda")
+        tab = torch.from_numpy(dp["block_table"]).to("cuda")
+        idx = torch.from_numpy(d["block_indices"]).to("cuda")
+        slots = idx.shape[2]
+        nsel = int((d["block_indices"] >= 0).sum())
+        meta = idx.numel() * 4 + nsel * 4 + sl.numel() * 4
+        call_args = lambda ns, ws: bsa.bsattn_decode_gqa_paged(q, k, v, sl, tab, idx, num_splits=ns,
+                                                               out=out, workspace=ws)
+    ns = bsa.bsattn_decode_default_splits(cfg.B, cfg.Hq, cfg.Hkv, slots, cfg.D)
+    ws_bytes = bsa.bsattn_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.D, ns)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    # algorithmic bytes: selected K and V tokens, q, out, and the selection metadata
+    algo_bytes = sel_tokens * 2 * cfg.D * 2 + q.numel() * 2 + out.numel() * 2 + meta
 
     def call():
-        bsa.bsattn_decode_gqa(q, k, v, cu, idx, num_splits=ns, out=out, workspace=ws)
+        call_args(ns, ws)
 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    times = []
-    for _ in range(steps):
-        # evict the selected K/V from the last-level cache with a read-only pass
-        torch.sum(flush, dim=0, keepdim=True, out=sink)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        times.append((a, b))
-    torch.cuda.synchronize()
+    times = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    gc.collect()
+    gc.disable()   # no collector pause between a call's start event and its launch
+    try:
+        for a, b in times:
+            # evict the selected K/V from the last-level cache with a read-only pass
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     ms = [a.elapsed_time(b) for a, b in times]
     avg = sum(ms) / len(ms)
     return {"cfg": cfg, "ns": ns, "algo_bytes": algo_bytes, "sel_tokens": sel_tokens,
             "ms_avg": avg, "ms_median": statistics.median(ms), "inputs": d}
+
+
+def bench_prefill_chunk(steps: int, warmup: int):
+    """Chunked prefill: the last 1024 queries of C2's 4096-token context (Sq 1024,
+    Sk 4096), C2's top-16/tril/diagonal mask rows for those query blocks."""
+    torch = _torch()
+    import block_sparse_attention_amd as bsa
+    from block_sparse_attention_amd import inputs as gen
+
+    cfg = gen.CONFIGS["C2"]
+    Sq = 1024
+    nbq = Sq // 64
+    inp = gen.prefill_inputs(cfg, 0)
+    # C2's mask from the library's own builder, then its last nbq block rows
+    scores = torch.from_numpy(inp["scores"]).to("cuda")
+    m_full = bsa.bsattn_build_mask_topk(scores, cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
+    mt = m_full[:, :, cfg.nb - nbq:, :].contiguous()
+    q = _gpu_bf16(np.ascontiguousarray(inp["q"][:, :, cfg.S - Sq:, :]))
+    k, v = _gpu_bf16(inp["k"]), _gpu_bf16(inp["v"])
+    out = torch.empty_like(q)
+    active = int((mt != 0).sum().item())
+    flops = active * FLOP_PER_BLOCK(cfg.D)
+
+    def call():
+        bsa.bsattn_fwd_chunk(q, k, v, mt, True, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"Sq": Sq, "Sk": cfg.S, "active": active, "flops": flops, "ms": ms, "cfg": cfg}
 
 
 def _blas_threads() -> int:
@@ -260,6 +336,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg (profiling runs)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the mask-form / paged decode and chunked-prefill measurements")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 10 times (counter calibration)")
     args = ap.parse_args(argv)
@@ -350,6 +428,34 @@ def main(argv=None):
         }
         if not args.no_cpu:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(dres)
+
+    if not args.no_next:
+        # the next rows of the hot path, each measured the same way as its base row
+        nxt = {}
+        if not args.no_decode:
+            for form in ("mask", "paged"):
+                r = bench_decode(args.decode_steps, 5, form=form, base=dres["inputs"])
+                gb = r["algo_bytes"] / (r["ms_avg"] * 1e-3) / 1e9
+                nxt[f"decode_{form}"] = {
+                    "workload": "C5 sparse GQA decode, " + (
+                        "mask form: block_mask [8, 8, 512]" if form == "mask"
+                        else "paged KV cache: 256-token pages in a shuffled order, block_table [8, 128]"),
+                    "value": round(gb, 2), "unit": "GB/s", "ms_per_call_avg": round(r["ms_avg"], 5),
+                    "ms_per_call_median": round(r["ms_median"], 5), "num_splits": r["ns"],
+                    "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBPS,
+                                 "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBPS, 4),
+                                 "bytes_per_call": r["algo_bytes"]}}
+        pc = bench_prefill_chunk(max(20, args.steps // 4), 5)
+        tf = pc["flops"] / (pc["ms"] * 1e-3) / 1e12
+        nxt["prefill_chunk"] = {
+            "workload": f"chunked prefill: the last {pc['Sq']} of {pc['Sk']} positions of C2 "
+                        f"(B2 H16 D64, its top-16/tril/diagonal mask rows), causal",
+            "value": round(tf, 3), "unit": "TFLOP/s", "ms_per_launch": round(pc["ms"], 5),
+            "active_blocks": pc["active"],
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "flop_per_launch": pc["flops"]}}
+        line["next_rows"] = nxt
 
     if not args.no_cpu:
         cb = cpu_baseline_prefill(res, args.cpu_budget)

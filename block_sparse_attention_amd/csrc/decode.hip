@@ -130,8 +130,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int nslots = a.max_sel;
   const int bps = nslots / ns;
   const int rem = nslots % ns;
-  const int my_len = bps + (sid < rem ? 1 : 0);
-  const int my_start = bps * sid + min(sid, rem);
+  // Index forms: a contiguous range of the (compact, -1 padded) list.  Mask
+  // form: every ns-th column starting at sid, so the selected blocks of a
+  // row spread evenly over the splits wherever they sit in the row.
+  const bool strided = MODE == kDecodeMask;
+  const int my_len = strided ? (nslots - sid + ns - 1) / ns : bps + (sid < rem ? 1 : 0);
+  const int my_start = strided ? sid : bps * sid + min(sid, rem);
+  const int slot_step = strided ? ns : 1;
   const int nper = my_len > w ? (my_len - w + kWaves - 1) / kWaves : 0;
 
   const uint32_t rsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens
@@ -275,10 +280,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   };
 
   for (int c0 = 0; c0 < nper; c0 += kWave) {
-    // this wave's next 64 slots: lane j holds slot my_start + w + kWaves * (c0 + j)
+    // this wave's next 64 slots: lane j holds slot my_start + slot_step * (w + kWaves * (c0 + j))
     int bv = -1;
     if (c0 + lane < nper) {
-      const int slot = my_start + w + kWaves * (c0 + lane);
+      const int slot = my_start + slot_step * (w + kWaves * (c0 + lane));
       if constexpr (MODE == kDecodeMask) bv = a.block_mask[sel_row + slot] ? slot : -1;
       else bv = a.block_indices[sel_row + slot];
     }

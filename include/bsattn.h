@@ -210,8 +210,9 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
  *                ignored).
  * Everything else (q, k, v, cu_seqlens_k, out, the split count, workspace,
  * GQA head mapping, the merge) is as in bsattn_decode_gqa, with num_blocks
- * in the place of max_selected_blocks: the slots cut into num_splits ranges
- * are the mask's columns.
+ * in the place of max_selected_blocks, except that the mask's columns are
+ * dealt to the splits round-robin (split s takes columns s, s + num_splits,
+ * ...), which spreads a row's selected blocks evenly over the splits.
  * Errors as bsattn_decode_gqa (num_blocks <= 0 or num_splits > num_blocks:
  * SHAPE).
  */
