@@ -7,10 +7,13 @@ runs inside the forward kernel).  The default workload is B2 H16 S4096 D64
 with a top-16 mask of N(0,1) block scores, tril, diagonal forced.
 
 Printed (one JSON line):
-* value      — active-block TFLOP/s of the whole step: sum over active blocks of
-               4*64*64*D flop, divided by the measured time per step;
+* value      — active-block TFLOP/s of the whole step (mask build + forward):
+               sum over active blocks of 4*64*64*D flop, divided by the
+               measured time per step;
 * roofline   — the forward kernel alone against the bf16 dense MFMA peak, its
                time taken per launch with HIP events on the launch stream;
+* fused_step_ms — the same step as one launch (bsattn_fwd_topk: row
+               selection inside the forward kernel), for comparison;
 * decode     — split-KV sparse GQA decode (batch 8, 32 query heads over 8 KV
                heads, D 128, KV lengths U[4096, 32768], up to 64 selected
                blocks): algorithmic HBM bytes per call over its time, with the
@@ -24,6 +27,8 @@ Printed (one JSON line):
                workload on this host.
 
 Inputs are synthetic (seeded generator) and resident in HBM before timing.
+Before its warm-up steps each leg runs its step untimed for half a second, so
+that the clocks have left the idle state the input generation leaves them in.
 """
 from __future__ import annotations
 
@@ -111,11 +116,6 @@ def bench_prefill(cfg_name: str, steps: int, warmup: int):
     flops = active * FLOP_PER_BLOCK(cfg.D)
     useful = (active - diag_blocks) * FLOP_PER_BLOCK(cfg.D) + diag_blocks * FLOP_PER_BLOCK(cfg.D) * 2080 / 4096
 
-    for _ in range(warmup):
-        build_mask()
-        bsa.bsattn_fwd(q, k, v, mask, cfg.is_causal, out=out)
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
 
     def timed(fn, n):
@@ -131,21 +131,48 @@ def bench_prefill(cfg_name: str, steps: int, warmup: int):
         return a.elapsed_time(b) / n
 
     def step():
+        # the whole hot path: the block mask from the scores, then the forward
+        # pass on it (per-row compaction inside the forward kernel)
         build_mask()
         bsa.bsattn_fwd(q, k, v, mask, cfg.is_causal, out=out)
 
-    # the timed region: `steps` whole steps (mask build + forward)
+    def step_fused():
+        # the same path in one launch: row selection, compaction and forward
+        if cfg.mask_kind == "topk":
+            bsa.bsattn_fwd_topk(q, k, v, scores, cfg.topk, cfg.dense_last_two_rows,
+                                cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask)
+        else:
+            bsa.bsattn_fwd_threshold(q, k, v, scores, cfg.threshold, cfg.dense_last_two_rows,
+                                     cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask)
+
+    _settle(step)
+    for _ in range(warmup):
+        step()
+    # the timed region: `steps` whole steps
     wall0 = time.perf_counter()
     ms_per_step = timed(step, steps)
     wall = time.perf_counter() - wall0
-    # the forward kernel alone and the mask build alone, back to back, for the roofline
+    # the forward kernel alone and the mask build alone, back to back, for the
+    # roofline; and the one-launch form of the same step
     fwd_avg = timed(lambda: bsa.bsattn_fwd(q, k, v, mask, cfg.is_causal, out=out), steps)
     mask_avg = timed(build_mask, steps)
+    fused = timed(step_fused, steps)
     return {
         "cfg": cfg, "active": active, "density": active / causal_blocks, "flops": flops,
         "useful_flops": useful, "ms_per_step": ms_per_step, "wall_s": wall,
-        "fwd_ms_avg": fwd_avg, "mask_ms_avg": mask_avg, "inputs": inp, "mask": m,
+        "fused_ms": fused, "fwd_ms_avg": fwd_avg, "mask_ms_avg": mask_avg,
+        "inputs": inp, "mask": m,
     }
+
+
+def _settle(fn, seconds: float = 0.5):
+    """Run fn back to back, untimed, for about `seconds` of wall time."""
+    torch = _torch()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
 
 
 def _selected_tokens(d, cfg):
@@ -211,6 +238,7 @@ def bench_decode(steps: int, warmup: int, form: str = "indices", base=None, page
     def call():
         call_args(ns, ws)
 
+    _settle(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -259,6 +287,7 @@ def bench_prefill_chunk(steps: int, warmup: int):
     def call():
         bsa.bsattn_fwd_chunk(q, k, v, mt, True, out=out)
 
+    _settle(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -407,6 +436,7 @@ def main(argv=None):
             "flop_per_launch": res["flops"],
             "useful_frac": round(res["useful_flops"] / (res["fwd_ms_avg"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
+        "fused_step_ms": round(res["fused_ms"], 5),
         "mask_build_ms_avg": round(res["mask_ms_avg"], 5),
     }
 

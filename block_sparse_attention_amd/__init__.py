@@ -19,6 +19,7 @@ __all__ = [
     "BLOCK", "BsattnError", "load_library", "bsattn_status_string", "bsattn_version",
     "bsattn_build_mask_topk", "bsattn_build_mask_threshold", "bsattn_mask_to_indices",
     "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices", "bsattn_fwd_chunk",
+    "bsattn_fwd_topk", "bsattn_fwd_threshold",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
     "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "EXPORTED_SYMBOLS",
 ]
@@ -32,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "bsattn_fwd", "bsattn_fwd_indices", "bsattn_decode_num_splits",
     "bsattn_decode_workspace_bytes", "bsattn_decode_gqa", "bsattn_decode_default_splits",
     "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "bsattn_fwd_chunk",
+    "bsattn_fwd_topk", "bsattn_fwd_threshold",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -61,6 +63,8 @@ _SIGS = {
     "bsattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_fwd_indices": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "bsattn_fwd_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_fwd_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "bsattn_fwd_threshold": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P, _P]),
     "bsattn_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -228,6 +232,52 @@ def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stre
         _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), B, H, S, D, int(bool(is_causal)),
         _ptr(out), _stream(stream)))
     return out
+
+
+def _fused_setup(q, k, v, scores, out, mask_out, write_mask):
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    nb = -(-S // BLOCK)
+    _dev(scores, "scores", torch.float32, 4)
+    if tuple(scores.shape) != (B, H, nb, nb):
+        raise ValueError("block scores must be [B, H, nb, nb]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, 4)
+    mask = mask_out
+    if mask is None and write_mask:
+        mask = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=q.device)
+    if mask is not None:
+        _dev(mask, "mask_out", torch.uint8, 4)
+        if tuple(mask.shape) != (B, H, nb, nb):
+            raise ValueError("mask_out must be [B, H, nb, nb]")
+    return B, H, S, D, out, mask
+
+
+def bsattn_fwd_topk(q, k, v, scores, topk: int, dense_last_two_rows: bool = False,
+                    force_diagonal: bool = True, is_causal: bool = True, out=None,
+                    mask_out=None, write_mask: bool = False, stream=None):
+    """Top-k mask build + compaction + forward in one launch (guide §3.1, §4).
+    The mask goes to mask_out when given (or to a new tensor with write_mask).
+    Returns out, or (out, mask) with write_mask."""
+    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask)
+    _check("bsattn_fwd_topk", load_library().bsattn_fwd_topk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, int(topk),
+        int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
+        _ptr(mask) if mask is not None else None, _ptr(out), _stream(stream)))
+    return (out, mask) if write_mask else out
+
+
+def bsattn_fwd_threshold(q, k, v, scores, threshold: float, dense_last_two_rows: bool = False,
+                         force_diagonal: bool = True, is_causal: bool = True, out=None,
+                         mask_out=None, write_mask: bool = False, stream=None):
+    """Threshold mask build + compaction + forward in one launch (guide §3.2, §4)."""
+    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask)
+    _check("bsattn_fwd_threshold", load_library().bsattn_fwd_threshold(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, float(threshold),
+        int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
+        _ptr(mask) if mask is not None else None, _ptr(out), _stream(stream)))
+    return (out, mask) if write_mask else out
 
 
 def bsattn_fwd_chunk(q, k, v, block_mask, is_causal: bool = True, out=None, stream=None):

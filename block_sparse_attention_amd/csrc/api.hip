@@ -138,9 +138,9 @@ size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
   return 0;
 }
 
-static bsattn_status fwd_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                const uint8_t* mask, const int32_t* idx, const int32_t* cnt,
-                                int B, int H, int Sq, int Sk, int D, int is_causal, uint16_t* out,
+// Shared checks and launch of the forward forms; `a` carries the
+// source-specific pointers (mask, list, or block scores).
+static bsattn_status fwd_common(PrefillArgs a, int B, int H, int Sq, int Sk, int D, int is_causal,
                                 hipStream_t stream) {
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
@@ -149,13 +149,18 @@ static bsattn_status fwd_common(const uint16_t* q, const uint16_t* k, const uint
   if (nblocks(Sk) > 65535 || prefill_lds_bytes(D, nblocks(Sk)) > kMaxLdsBytes)
     return BSATTN_ERR_UNSUPPORTED;
   if (!fits_elems((long double)B * H * Sk * D)) return BSATTN_ERR_SHAPE;
-  PrefillArgs a{};
-  a.q = q; a.k = k; a.v = v; a.out = out;
-  a.mask = mask; a.idx = idx; a.cnt = cnt;
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
   a.nbq = nblocks(Sq); a.nbk = nblocks(Sk);
   a.causal = is_causal ? 1 : 0;
   return launch_prefill(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+static PrefillArgs fwd_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                            int src) {
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.src = src;
+  return a;
 }
 
 bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -167,23 +172,59 @@ bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
     const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
     if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
   }
-  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, S, S, D, is_causal, out,
-                    as_hip(stream));
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcMask);
+  a.mask = block_mask;
+  return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 
 bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const uint8_t* block_mask, int B, int H, int Sq, int Sk, int D,
                                int is_causal, uint16_t* out, bsattn_stream_t stream) {
   if (!q || !k || !v || !block_mask || !out) return BSATTN_ERR_NULL;
-  return fwd_common(q, k, v, block_mask, nullptr, nullptr, B, H, Sq, Sk, D, is_causal, out,
-                    as_hip(stream));
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcMask);
+  a.mask = block_mask;
+  return fwd_common(a, B, H, Sq, Sk, D, is_causal, as_hip(stream));
 }
 
 bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const int32_t* idx, const int32_t* cnt, int B, int H, int S,
                                  int D, int is_causal, uint16_t* out, bsattn_stream_t stream) {
   if (!q || !k || !v || !idx || !cnt || !out) return BSATTN_ERR_NULL;
-  return fwd_common(q, k, v, nullptr, idx, cnt, B, H, S, S, D, is_causal, out, as_hip(stream));
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcList);
+  a.idx = idx; a.cnt = cnt;
+  return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
+}
+
+// The fused forms hold a row's order keys in registers, 4 per lane.
+static bool fused_nb_ok(int D, int S) {
+  (void)D;
+  return nblocks(S) <= 256;
+}
+
+bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* block_scores, int B, int H, int S, int D, int topk,
+                              int dense_last_two_rows, int force_diagonal, int is_causal,
+                              uint8_t* mask_out, uint16_t* out, bsattn_stream_t stream) {
+  if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
+  if (S > 0 && (topk < 0 || topk > nblocks(S))) return BSATTN_ERR_SHAPE;
+  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcTopk);
+  a.scores = block_scores; a.mask_out = mask_out; a.topk = topk;
+  a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;
+  return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
+}
+
+bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* block_scores, int B, int H, int S, int D,
+                                   float threshold, int dense_last_two_rows, int force_diagonal,
+                                   int is_causal, uint8_t* mask_out, uint16_t* out,
+                                   bsattn_stream_t stream) {
+  if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
+  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcThreshold);
+  a.scores = block_scores; a.mask_out = mask_out; a.threshold = threshold;
+  a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;
+  return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 
 int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,

@@ -14,14 +14,28 @@ hipError_t launch_mask_threshold(const float* scores, int B, int H, int nb, floa
 hipError_t launch_compact(const uint8_t* mask, int B, int H, int nb, int causal, int32_t* idx,
                           int32_t* cnt, hipStream_t stream);
 
+// Where a forward work item gets its block list from.
+enum PrefillSource {
+  kSrcMask = 0,       // mask [B,H,nbq,nbk]
+  kSrcList = 1,       // idx [B,H,nbq,nbk] + cnt [B,H,nbq]
+  kSrcTopk = 2,       // block scores [B,H,nb,nb]: top-k row selection in the prologue
+  kSrcThreshold = 3,  // block scores [B,H,nb,nb]: score > threshold in the prologue
+};
+
 struct PrefillArgs {
   const uint16_t* q;     // [B,H,Sq,D]
   const uint16_t* k;     // [B,H,Sk,D]
   const uint16_t* v;     // [B,H,Sk,D]
   uint16_t* out;         // [B,H,Sq,D]
-  const uint8_t* mask;   // [B,H,nbq,nbk] mask form, or nullptr
-  const int32_t* idx;    // [B,H,nbq,nbk] list form, or nullptr
-  const int32_t* cnt;    // [B,H,nbq]
+  const uint8_t* mask;   // kSrcMask
+  const int32_t* idx;    // kSrcList
+  const int32_t* cnt;    // kSrcList
+  const float* scores;   // kSrcTopk / kSrcThreshold (square: Sq = Sk)
+  uint8_t* mask_out;     // kSrcTopk / kSrcThreshold: the built mask, or nullptr
+  int topk;
+  float threshold;
+  int dense2, diag;      // dense last two rows; force the diagonal
+  int src;               // PrefillSource
   int B, H, Sq, Sk, D, nbq, nbk;   // Sq <= Sk: the queries are the last Sq positions
   int causal;
 };

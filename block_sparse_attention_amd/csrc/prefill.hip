@@ -175,7 +175,18 @@ struct Probs {
   u32x4 p[2 * NT];
 };
 
-template <int D, int KS, bool CAUSAL, bool LIST>
+// Order key of column c with block score x: a larger key is a larger score,
+// and among equal scores the lower column; -0.0 and +0.0 are equal scores.
+__device__ __forceinline__ uint64_t rank_key(float x, int c) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+}
+
+constexpr int kMaxKeyChunks = 4;   // fused row selection handles up to 256 key blocks
+
+template <int D, int KS, bool CAUSAL, int SRC>
 __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, int map_mode,
                                                                   int group) {
   using C = Cfg<D, KS>;
@@ -226,11 +237,19 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       qf[s] = *(const u32x4*)(Q + (int64_t)qr * D + 16 * s + 8 * h);
   }
 
-  // ---- compact this query block's mask row (or list) into LDS ----
+  // ---- this query block's list of key blocks, ascending, into LDS ----
+  // From a mask row, a given list, or (fused) a block-score row: the row is
+  // selected here as the mask builders select it (TileLang block-sparse guide
+  // §3.1 top-k, §3.2 threshold: optional dense last two rows, tril, then the
+  // forced diagonal of the XAttention guide), written out if asked, and
+  // compacted in the same pass.
+  // Fused forms: the selected columns of the row, one bit each, written to the
+  // mask output after the forward pass so the stores stay off the first waits.
+  uint64_t selbits[kMaxKeyChunks] = {};
   if (w == 0) {
     int count = 0;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    if constexpr (LIST) {
+    if constexpr (SRC == kSrcList) {
       const int64_t row = (int64_t)bh * nbq + i;
       const int nl = max(0, min(a.cnt[row], nbk));
       const int32_t* src = a.idx + row * nbk;
@@ -242,11 +261,74 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
         count += __popcll(bits);
       }
-    } else {
+    } else if constexpr (SRC == kSrcMask) {
       const uint8_t* mrow = a.mask + ((int64_t)bh * nbq + i) * nbk;
       for (int c0 = 0; c0 < lim; c0 += kWave) {
         const int j = c0 + lane;
         const bool ok = j < lim && mrow[j] != 0;
+        const uint64_t bits = wave_ballot(ok);
+        if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
+        count += __popcll(bits);
+      }
+    } else {
+      // square problem: nbq = nbk = nb
+      const int64_t row = (int64_t)bh * nbk + i;
+      const float* x = a.scores + row * nbk;
+      const bool dense_row = a.dense2 && i >= nbk - 2;
+      const bool all = dense_row || (SRC == kSrcTopk && a.topk >= nbk);
+      const bool none = SRC == kSrcTopk && a.topk == 0 && !dense_row;
+      const bool ranked = SRC == kSrcTopk && !all && !none;
+      // Top-k by a bitwise radix select over the wave: the row's order keys
+      // (distinct: ties are broken by the column) sit in registers, lane l
+      // holding columns l, l+64, ...; walking the key bits from the top, the
+      // prefix of the topk-th largest key is fixed one bit at a time from
+      // ballot counts, stopping as soon as the keys matching the prefix are
+      // exactly the ones still needed.  A column is selected when its key,
+      // cut to the decided bits, is at least that prefix.
+      uint64_t key[kMaxKeyChunks];
+      uint64_t hm = 0, prefix = 0;
+      if (ranked) {
+#pragma unroll
+        for (int u = 0; u < kMaxKeyChunks; ++u) {
+          const int c = 64 * u + lane;
+          key[u] = c < nbk ? rank_key(x[c], c) : 0ull;   // 0 is below every real key
+        }
+        int want = a.topk;
+        for (int bit = 63; bit >= 0; --bit) {
+          const uint64_t m = ~0ull << bit;
+          const uint64_t target = prefix | (1ull << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int u = 0; u < kMaxKeyChunks; ++u)
+            if (64 * u < nbk) cnt += __popcll(wave_ballot((key[u] & m) == target));
+          int cand;
+          if (cnt >= want) {
+            prefix = target;
+            cand = cnt;
+          } else {
+            want -= cnt;
+            cand = 0;
+#pragma unroll
+            for (int u = 0; u < kMaxKeyChunks; ++u)
+              if (64 * u < nbk) cand += __popcll(wave_ballot((key[u] & m) == prefix));
+          }
+          hm = m;
+          if (cand == want) break;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMaxKeyChunks; ++u) {
+        const int j = 64 * u + lane;
+        if (64 * u >= nbk) break;
+        bool sel = false;
+        if (j < nbk && j <= i) {   // tril: columns above the diagonal are never selected
+          if (all) sel = true;
+          else if (SRC == kSrcThreshold) sel = dense_row || x[j] > a.threshold;
+          else if (ranked) sel = (key[u] & hm) >= prefix;
+          if (a.diag && j == i) sel = true;
+        }
+        selbits[u] = wave_ballot(sel);
+        const bool ok = sel && j < lim;
         const uint64_t bits = wave_ballot(ok);
         if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
         count += __popcll(bits);
@@ -652,6 +734,17 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     else finish(std::integral_constant<int, 1>{});
   }
   }
+
+  if constexpr (SRC == kSrcTopk || SRC == kSrcThreshold) {
+    if (w == 0 && a.mask_out) {
+      uint8_t* mo = a.mask_out + ((int64_t)bh * nbk + i) * nbk;
+#pragma unroll
+      for (int u = 0; u < kMaxKeyChunks; ++u) {
+        const int j = 64 * u + lane;
+        if (j < nbk) mo[j] = (uint8_t)((selbits[u] >> lane) & 1ull);
+      }
+    }
+  }
 }
 
 // Key splits per work item by head dim: at D = 64 two waves (all keys each)
@@ -666,7 +759,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 template <int D>
 constexpr int kKeySplits = D == 64 ? BSATTN_KS64 : BSATTN_KS128;
 
-template <int D, bool CAUSAL, bool LIST>
+template <int D, bool CAUSAL, int SRC>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   constexpr int KS = kKeySplits<D>;
   const int BH = a.B * a.H;
@@ -681,7 +774,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     group = g;
   }
   const size_t lds = lds_bytes<D, KS>(a.nbk);
-  auto kern = prefill_kernel<D, KS, CAUSAL, LIST>;
+  auto kern = prefill_kernel<D, KS, CAUSAL, SRC>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -699,14 +792,19 @@ size_t prefill_lds_bytes(int D, int nbk) {
   return D == 64 ? lds_bytes<64, kKeySplits<64>>(nbk) : lds_bytes<128, kKeySplits<128>>(nbk);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const bool list = a.mask == nullptr;
-  if (a.D == 64) {
-    if (a.causal) return list ? launch_t<64, true, true>(a, stream) : launch_t<64, true, false>(a, stream);
-    return list ? launch_t<64, false, true>(a, stream) : launch_t<64, false, false>(a, stream);
+template <int D, bool CAUSAL>
+hipError_t launch_src(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.src) {
+    case kSrcList: return launch_t<D, CAUSAL, kSrcList>(a, stream);
+    case kSrcTopk: return launch_t<D, CAUSAL, kSrcTopk>(a, stream);
+    case kSrcThreshold: return launch_t<D, CAUSAL, kSrcThreshold>(a, stream);
+    default: return launch_t<D, CAUSAL, kSrcMask>(a, stream);
   }
-  if (a.causal) return list ? launch_t<128, true, true>(a, stream) : launch_t<128, true, false>(a, stream);
-  return list ? launch_t<128, false, true>(a, stream) : launch_t<128, false, false>(a, stream);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.D == 64) return a.causal ? launch_src<64, true>(a, stream) : launch_src<64, false>(a, stream);
+  return a.causal ? launch_src<128, true>(a, stream) : launch_src<128, false>(a, stream);
 }
 
 }  // namespace bsattn

@@ -132,6 +132,29 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
                                  int D, int is_causal, uint16_t* out, bsattn_stream_t stream);
 
 /*
+ * The whole prefill hot path in one launch: each work item selects its
+ * query block's row from the fp32 block scores [B, H, nb, nb] exactly as
+ * bsattn_build_mask_topk / bsattn_build_mask_threshold do (guide §3.1 / §3.2:
+ * top-k with ties to the lower column, or score > threshold; optional dense
+ * last two rows; tril; forced diagonal), writes that row to mask_out when
+ * mask_out is not NULL (uint8 0/1 [B, H, nb, nb], byte-identical to the
+ * builders' output), compacts it, and runs the forward pass of bsattn_fwd on
+ * it.  q/k/v/out and is_causal as bsattn_fwd.
+ * Errors: as bsattn_fwd and the builders (topk < 0 or topk > nb: SHAPE);
+ * nb > 256 (S > 16384: the row's keys are held in registers) is UNSUPPORTED,
+ * where the two-launch path (builder, then bsattn_fwd) applies.
+ */
+bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* block_scores, int B, int H, int S, int D, int topk,
+                              int dense_last_two_rows, int force_diagonal, int is_causal,
+                              uint8_t* mask_out, uint16_t* out, bsattn_stream_t stream);
+bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* block_scores, int B, int H, int S, int D,
+                                   float threshold, int dense_last_two_rows, int force_diagonal,
+                                   int is_causal, uint8_t* mask_out, uint16_t* out,
+                                   bsattn_stream_t stream);
+
+/*
  * Forward pass for a chunk of queries at the end of a longer context
  * (chunked or incremental prefill): q and out bfloat16 [B, H, Sq, D], k and
  * v bfloat16 [B, H, Sk, D] with Sq <= Sk, block_mask uint8

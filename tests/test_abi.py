@@ -90,6 +90,20 @@ def test_decode_validates_on_host():
     assert lib.bsattn_decode_workspace_bytes(0, 8, 128, 2) == 0
 
 
+def test_fused_fwd_validates_on_host():
+    lib = _lib()
+    F = FAKE
+    assert lib.bsattn_fwd_topk(None, F, F, F, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None) == 1
+    assert lib.bsattn_fwd_topk(F, F, F, None, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None) == 1
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, 5, 0, 1, 1, None, F, None) == 2   # topk > nb
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, -1, 0, 1, 1, None, F, None) == 2
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 96, 2, 0, 1, 1, None, F, None) == 3
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 64 * 257, 64, 2, 0, 1, 1, None, F, None) == 3
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 1, 64 * 257, 64, 0.5, 0, 1, 1, None, F, None) == 3
+    assert lib.bsattn_fwd_threshold(F, F, F, None, 1, 1, 256, 64, 0.5, 0, 1, 1, None, F, None) == 1
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 0, 1, 256, 64, 0.5, 0, 1, 1, None, F, None) == 2
+
+
 def test_chunk_fwd_validates_on_host():
     lib = _lib()
     F = FAKE
