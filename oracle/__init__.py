@@ -16,6 +16,10 @@ Modules:
   over the token-level expansion of the block mask (same guide §5, §4.5),
   and sparse GQA decode over selected KV blocks (same guide §6–§6.2).
 * ``oracle.heuristic`` — the split-count heuristic (same guide §6.3).
+* ``oracle.xattn``     — the XAttention block-importance estimator: stride
+  reshape (inverse mode), block sums of the reshaped softmax, and selection
+  by cumulative weight with sink and diagonal (XAttention guide, "algorithm
+  flow" phases 1-3).
 
 Every function is pinned by tests against library routines, brute force,
 closed forms and invariants (``tests/test_oracle_*.py``).
