@@ -21,7 +21,9 @@ __all__ = [
     "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices", "bsattn_fwd_chunk",
     "bsattn_fwd_topk", "bsattn_fwd_threshold",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
-    "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "EXPORTED_SYMBOLS",
+    "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
+    "bsattn_xattn_workspace_bytes", "bsattn_xattn_block_sums", "bsattn_build_mask_cumulative",
+    "bsattn_xattn_estimate", "EXPORTED_SYMBOLS",
 ]
 
 BLOCK = 64
@@ -33,7 +35,8 @@ EXPORTED_SYMBOLS = (
     "bsattn_fwd", "bsattn_fwd_indices", "bsattn_decode_num_splits",
     "bsattn_decode_workspace_bytes", "bsattn_decode_gqa", "bsattn_decode_default_splits",
     "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "bsattn_fwd_chunk",
-    "bsattn_fwd_topk", "bsattn_fwd_threshold",
+    "bsattn_fwd_topk", "bsattn_fwd_threshold", "bsattn_xattn_workspace_bytes",
+    "bsattn_xattn_block_sums", "bsattn_build_mask_cumulative", "bsattn_xattn_estimate",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -72,6 +75,11 @@ _SIGS = {
     "bsattn_decode_gqa_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_decode_gqa_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _P, _P, _Z, _P]),
+    "bsattn_xattn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "bsattn_xattn_block_sums": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _Z, _P]),
+    "bsattn_build_mask_cumulative": (_I, [_P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P]),
+    "bsattn_xattn_estimate": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P, _P, _P,
+                                   _Z, _P]),
 }
 
 
@@ -417,3 +425,86 @@ def bsattn_decode_gqa_paged(q, k_cache, v_cache, cache_seqlens, block_table, blo
         _ptr(block_indices), B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1], max_sel,
         ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out
+
+
+# ---- XAttention block-importance estimator ----
+
+def bsattn_xattn_workspace_bytes(B: int, H: int, Sq: int, Sk: int, stride: int) -> int:
+    return int(load_library().bsattn_xattn_workspace_bytes(B, H, Sq, Sk, stride))
+
+
+def _xattn_qk(q, k):
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(k, "k", torch.bfloat16, 4)
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q [B, H, Sq, D] and k [B, H, Sk, D] must agree on B, H, D")
+    return B, H, Sq, k.shape[2], D
+
+
+def _xattn_ws(B, H, Sq, Sk, stride, workspace, device):
+    torch = _torch()
+    need = bsattn_xattn_workspace_bytes(B, H, Sq, Sk, stride)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def bsattn_xattn_block_sums(q, k, stride: int = 8, norm: float = 1.0, is_causal: bool = True,
+                            out=None, workspace=None, stream=None):
+    """XAttention block estimate (XAttention guide, phases 1-2): q bf16 [B,H,Sq,D],
+    k bf16 [B,H,Sk,D] -> float32 block sums [B,H,ceil(Sq/64),ceil(Sk/64)]."""
+    torch = _torch()
+    B, H, Sq, Sk, D = _xattn_qk(q, k)
+    nbq, nbk = -(-Sq // BLOCK), -(-Sk // BLOCK)
+    if out is None:
+        out = torch.empty((B, H, nbq, nbk), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 4)
+    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device)
+    _check("bsattn_xattn_block_sums", load_library().bsattn_xattn_block_sums(
+        _ptr(q), _ptr(k), B, H, Sq, Sk, D, int(stride), float(norm), int(bool(is_causal)),
+        _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def bsattn_build_mask_cumulative(block_sums, threshold: float = 0.9, keep_sink: bool = True,
+                                 keep_diagonal: bool = True, is_causal: bool = True, out=None,
+                                 stream=None):
+    """float32 [B,H,nbq,nbk] -> uint8 0/1 mask, selection by cumulative weight
+    (XAttention guide, block-selection section)."""
+    torch = _torch()
+    _dev(block_sums, "block_sums", torch.float32, 4)
+    B, H, nbq, nbk = block_sums.shape
+    if out is None:
+        out = torch.empty((B, H, nbq, nbk), dtype=torch.uint8, device=block_sums.device)
+    _dev(out, "out", torch.uint8, 4)
+    _check("bsattn_build_mask_cumulative", load_library().bsattn_build_mask_cumulative(
+        _ptr(block_sums), B, H, nbq, nbk, float(threshold), int(bool(keep_sink)),
+        int(bool(keep_diagonal)), int(bool(is_causal)), _ptr(out), _stream(stream)))
+    return out
+
+
+def bsattn_xattn_estimate(q, k, stride: int = 8, norm: float = 1.0, threshold: float = 0.9,
+                          keep_sink: bool = True, keep_diagonal: bool = True,
+                          is_causal: bool = True, block_sums=None, write_sums: bool = False,
+                          out=None, workspace=None, stream=None):
+    """The whole estimator (XAttention guide, phases 1-3) -> uint8 mask [B,H,nbq,nbk],
+    or (mask, block_sums) when block_sums is given or write_sums is set."""
+    torch = _torch()
+    B, H, Sq, Sk, D = _xattn_qk(q, k)
+    nbq, nbk = -(-Sq // BLOCK), -(-Sk // BLOCK)
+    if out is None:
+        out = torch.empty((B, H, nbq, nbk), dtype=torch.uint8, device=q.device)
+    _dev(out, "out", torch.uint8, 4)
+    if block_sums is None and write_sums:
+        block_sums = torch.empty((B, H, nbq, nbk), dtype=torch.float32, device=q.device)
+    if block_sums is not None:
+        _dev(block_sums, "block_sums", torch.float32, 4)
+    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device)
+    _check("bsattn_xattn_estimate", load_library().bsattn_xattn_estimate(
+        _ptr(q), _ptr(k), B, H, Sq, Sk, D, int(stride), float(norm), float(threshold),
+        int(bool(keep_sink)), int(bool(keep_diagonal)), int(bool(is_causal)),
+        None if block_sums is None else _ptr(block_sums), _ptr(out), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out if block_sums is None else (out, block_sums)

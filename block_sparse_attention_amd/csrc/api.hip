@@ -337,3 +337,115 @@ bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache
 }
 
 }  // extern "C"
+
+// ---- XAttention block-importance estimator ----
+
+namespace {
+
+bool xattn_shape_ok(int B, int H, int Sq, int Sk, int stride) {
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return false;
+  if (stride <= 0 || Sq % stride != 0 || Sk % stride != 0) return false;
+  if ((Sk - Sq) % BSATTN_BLOCK != 0) return false;
+  return (long long)B * H <= 65535;
+}
+
+bool xattn_stride_ok(int stride) { return stride == 4 || stride == 8 || stride == 16; }
+
+size_t xattn_sums_bytes(int B, int H, int Sq, int Sk) {
+  return (size_t)B * H * nblocks(Sq) * nblocks(Sk) * sizeof(float);
+}
+
+bsattn_status xattn_sums_common(const uint16_t* q, const uint16_t* k, int B, int H, int Sq, int Sk,
+                                int D, int stride, float norm, int is_causal, float* block_sums,
+                                void* workspace, size_t workspace_bytes, bool sums_in_ws,
+                                hipStream_t stream) {
+  if (!xattn_shape_ok(B, H, Sq, Sk, stride)) return BSATTN_ERR_SHAPE;
+  if (!(norm > 0.0f) || !isfinite(norm)) return BSATTN_ERR_SHAPE;
+  if (!head_dim_ok(D) || !xattn_stride_ok(stride)) return BSATTN_ERR_UNSUPPORTED;
+  if (nblocks(Sk) > xattn_max_key_blocks()) return BSATTN_ERR_UNSUPPORTED;
+  if (!fits_elems((long double)B * H * Sk * D)) return BSATTN_ERR_SHAPE;
+  const size_t lse_bytes = align_up(xattn_lse_bytes(B, H, Sq, Sk, stride));
+  const size_t need = lse_bytes + align_up(xattn_sums_bytes(B, H, Sq, Sk));
+  if (!workspace || workspace_bytes < need) return BSATTN_ERR_WORKSPACE;
+  XattnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.lse = (float*)workspace;
+  a.block_sums = sums_in_ws ? (float*)((char*)workspace + lse_bytes) : block_sums;
+  a.scale_log2 = (float)(1.4426950408889634 / (sqrt((double)D) * stride * (double)norm));
+  a.BH = B * H;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.D = D;
+  a.stride = stride;
+  a.nbq = nblocks(Sq);
+  a.nbk = nblocks(Sk);
+  a.causal = is_causal ? 1 : 0;
+  return launch_xattn_block_sums(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
+}
+
+bsattn_status cumulative_check(int B, int H, int nbq, int nbk) {
+  if (B <= 0 || H <= 0 || nbq <= 0 || nbk < nbq) return BSATTN_ERR_SHAPE;
+  if ((long long)B * H * nbq > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (nbk > xattn_max_key_blocks()) return BSATTN_ERR_UNSUPPORTED;
+  return BSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bsattn_xattn_workspace_bytes(int B, int H, int Sq, int Sk, int stride) {
+  if (!xattn_shape_ok(B, H, Sq, Sk, stride)) return 0;
+  return align_up(xattn_lse_bytes(B, H, Sq, Sk, stride)) +
+         align_up(xattn_sums_bytes(B, H, Sq, Sk));
+}
+
+bsattn_status bsattn_xattn_block_sums(const uint16_t* q, const uint16_t* k, int B, int H, int Sq,
+                                      int Sk, int D, int stride, float norm, int is_causal,
+                                      float* block_sums, void* workspace, size_t workspace_bytes,
+                                      bsattn_stream_t stream) {
+  if (!q || !k || !block_sums) return BSATTN_ERR_NULL;
+  return xattn_sums_common(q, k, B, H, Sq, Sk, D, stride, norm, is_causal, block_sums, workspace,
+                           workspace_bytes, false, as_hip(stream));
+}
+
+bsattn_status bsattn_build_mask_cumulative(const float* block_sums, int B, int H, int nbq, int nbk,
+                                           float threshold, int keep_sink, int keep_diagonal,
+                                           int is_causal, uint8_t* mask, bsattn_stream_t stream) {
+  if (!block_sums || !mask) return BSATTN_ERR_NULL;
+  const bsattn_status st = cumulative_check(B, H, nbq, nbk);
+  if (st != BSATTN_OK) return st;
+  return launch_mask_cumulative(block_sums, B, H, nbq, nbk, threshold, keep_sink ? 1 : 0,
+                                keep_diagonal ? 1 : 0, is_causal ? 1 : 0, mask,
+                                as_hip(stream)) == hipSuccess
+             ? BSATTN_OK
+             : BSATTN_ERR_HIP;
+}
+
+bsattn_status bsattn_xattn_estimate(const uint16_t* q, const uint16_t* k, int B, int H, int Sq,
+                                    int Sk, int D, int stride, float norm, float threshold,
+                                    int keep_sink, int keep_diagonal, int is_causal,
+                                    float* block_sums, uint8_t* mask, void* workspace,
+                                    size_t workspace_bytes, bsattn_stream_t stream) {
+  if (!q || !k || !mask) return BSATTN_ERR_NULL;
+  if (xattn_shape_ok(B, H, Sq, Sk, stride)) {
+    const bsattn_status st = cumulative_check(B, H, nblocks(Sq), nblocks(Sk));
+    if (st != BSATTN_OK) return st;
+  }
+  const bool in_ws = block_sums == nullptr;
+  const bsattn_status st =
+      xattn_sums_common(q, k, B, H, Sq, Sk, D, stride, norm, is_causal, block_sums, workspace,
+                        workspace_bytes, in_ws, as_hip(stream));
+  if (st != BSATTN_OK) return st;
+  const float* sums =
+      in_ws ? (const float*)((const char*)workspace + align_up(xattn_lse_bytes(B, H, Sq, Sk, stride)))
+            : block_sums;
+  return launch_mask_cumulative(sums, B, H, nblocks(Sq), nblocks(Sk), threshold, keep_sink ? 1 : 0,
+                                keep_diagonal ? 1 : 0, is_causal ? 1 : 0, mask,
+                                as_hip(stream)) == hipSuccess
+             ? BSATTN_OK
+             : BSATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -53,4 +53,63 @@ __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Order key of column c with score x: a larger key is a larger score, and
+// among equal scores the lower column; -0.0 and +0.0 are equal scores.  Every
+// key of a column below 2^32 - 1 is nonzero.
+__device__ __forceinline__ uint64_t rank_key(float x, int c) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+}
+
+// The score and column a rank_key encodes (a zero score comes back as +0.0).
+__device__ __forceinline__ float rank_key_score(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int rank_key_column(uint64_t key) {
+  return (int)(0xffffffffu - (uint32_t)key);
+}
+
+// ---- wave-level memory and matrix-core primitives ----
+
+// One wave-wide 16-byte-per-lane load straight into LDS: lane l reads
+// base + voff_l (base uniform, voff a per-lane byte offset) and its 16 bytes
+// go to LDS byte address lds + kLdsOff + 16 * l (M0 holds the uniform base).
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds), "i"(kLdsOff)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void barrier_raw() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t byte_addr) {
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((BSATTN_LDS bf16x4*)(uintptr_t)byte_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t byte_addr) {
+  return *(const BSATTN_LDS u32x4*)(uintptr_t)byte_addr;
+}
+
 }  // namespace bsattn

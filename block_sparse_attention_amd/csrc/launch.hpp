@@ -69,4 +69,22 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// XAttention block-importance estimate.
+struct XattnArgs {
+  const uint16_t* q;    // [B,H,Sq,D]
+  const uint16_t* k;    // [B,H,Sk,D]
+  float* lse;           // workspace [B*H, Sq/stride, nbk]: per (reshaped row, key block) log2-sum-exp2
+  float* block_sums;    // [B,H,nbq,nbk]
+  float scale_log2;     // log2(e) / (sqrt(D) * stride * norm)
+  int BH, Sq, Sk, D, stride, nbq, nbk;
+  int causal;
+  int ntc;              // set by the launcher: 128-wide reshaped column tiles
+};
+hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream);
+hipError_t launch_mask_cumulative(const float* sums, int B, int H, int nbq, int nbk, float threshold,
+                                  int keep_sink, int keep_diag, int causal, uint8_t* mask,
+                                  hipStream_t stream);
+size_t xattn_lse_bytes(int B, int H, int Sq, int Sk, int stride);
+int xattn_max_key_blocks();
+
 }  // namespace bsattn

@@ -71,14 +71,6 @@ __global__ __launch_bounds__(kTopkThreads) void mask_topk_kernel(const float* __
   }
 }
 
-// Order key of column c with score x: larger key <=> larger score, and among
-// equal scores the lower column.  -0.0 and +0.0 are equal scores.
-__device__ __forceinline__ uint64_t rank_key(float x, int c) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) == 0) u = 0;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
-}
 
 constexpr int kWaveRows = 4;        // rows per work-group, one wave each
 constexpr int kWaveMaxNb = 1024;    // rows up to this length use the one-wave kernel

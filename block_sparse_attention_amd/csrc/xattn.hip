@@ -1,0 +1,395 @@
+// XAttention block-importance estimator (gfx950): the block scores upstream
+// of the block mask (XAttention guide, "algorithm flow" phases 1-3).
+//
+// Stride reshape in inverse mode (the guide's stride-reshape section): with
+// stride s, reshaped key row t' is key rows t's .. t's+s-1 concatenated, and
+// reshaped query row r' is query rows r's+s-1 down to r's.  The reshaped
+// logit is therefore
+//     L[r', t'] = sum_j q[r's + s-1-j] . k[t's + j]  / (sqrt(D) * s * norm),
+// a GEMM with inner dimension s*D.  No reshaped copy is made: K' is K read
+// as [Sk/s, s*D] rows (contiguous), and Q' is Q read the same way with the s
+// sub-rows of each reshaped row taken in reverse, which is only a different
+// source address per 64-dimension chunk of the inner loop (the guide's fused
+// reshape-GEMM does the same with pointer arithmetic).
+//
+// Three kernels:
+// * xattn_lse_kernel: one 128 x 128 tile of L^T per work-group (4 waves, each
+//   64 x 64 from 32x32x16 bf16 MFMAs; operands stream HBM -> LDS by direct
+//   loads, double-buffered over 64-dimension chunks).  The tile's epilogue
+//   reduces every (reshaped row, 64-token key block) to the log2-sum-exp2 of
+//   its scaled logits and stores it.  Tiles are independent: the row softmax
+//   needs the whole row, and per-block log-sums let the next kernel normalise
+//   without a second pass over the GEMM.
+// * xattn_blocksum_kernel: per (query block, all key blocks): each reshaped
+//   row's log-normaliser from its block log-sums, then the block sums of the
+//   softmax weights (the guide's softmax + block-sum kernel description).
+// * mask_cumulative_kernel: per query-block row, block selection by
+//   cumulative weight (the guide's block-selection section): sink and
+//   diagonal kept, the rest ranked by weight and kept while the weight
+//   ranked above is below threshold * total.  Sums are float64, the total in
+//   ascending column order and the ranked sum in rank order, one term at a
+//   time; the ranking is a bitonic sort of order keys in LDS.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bsattn {
+
+namespace {
+
+constexpr int kXTile = 128;           // reshaped rows and columns per tile
+constexpr int kXThreads = 256;        // 4 waves, each 64 x 64 of the tile
+constexpr int kXChunk = 64;           // inner dimensions per LDS stage
+constexpr int kXOpBytes = kXTile * kXChunk * 2;   // one operand tile per stage: 16 KiB
+constexpr int kXStageBytes = 2 * kXOpBytes;       // K' then Q'
+constexpr int kXLdsBytes = 2 * kXStageBytes;      // two stages
+
+// 16-byte granule g of LDS row r (128 bytes) is stored at granule g ^ xswz(r):
+// the 32-row, 16-byte-per-lane operand reads then touch every bank once.
+__device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
+
+// Grid (row tiles x column tiles, B*H).  A tile whose columns all lie past
+// the causal limit of every row it holds is not computed.
+template <int D, int S>
+__global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
+  constexpr int kChunks = S * D / kXChunk;   // inner-dimension stages
+  constexpr int kBk = 64 / S;                // reshaped columns per 64-token key block
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int n = lane & 31;
+
+  const int bh = blockIdx.y;
+  const int ntc = a.ntc;
+  const int rt = blockIdx.x / ntc;
+  const int ct = blockIdx.x - rt * ntc;
+  const int rq = a.Sq / S, rk = a.Sk / S;          // reshaped lengths
+  const int past = (a.Sk - a.Sq) / S;             // reshaped causal offset
+  const int r0 = rt * kXTile, t0 = ct * kXTile;
+  if (a.causal && t0 > r0 + kXTile - 1 + past) return;   // the whole tile is masked
+
+  const uint16_t* __restrict__ Kh = a.k + (int64_t)bh * a.Sk * D;
+  const uint16_t* __restrict__ Qh = a.q + (int64_t)bh * a.Sq * D;
+
+  // DMA: instruction kk (0..15) of an operand tile covers its rows 8kk .. 8kk+7;
+  // lane l fills LDS granule l % 8 of row 8kk + l / 8 with the source granule
+  // that the swizzle puts there.  Wave w issues kk = w, w+4, w+8, w+12.
+  uint32_t voff_k[4], voff_q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (w + 4 * i) + (lane >> 3);
+    const int g = (lane & 7) ^ xswz(row);
+    const int kr = min(t0 + row, rk - 1);   // rows past the end re-read the last (masked later)
+    const int qr = min(r0 + row, rq - 1);   // rows past the end are never stored
+    voff_k[i] = (uint32_t)(((int64_t)kr * S * D + 8 * g) * 2);
+    voff_q[i] = (uint32_t)(((int64_t)qr * S * D + 8 * g) * 2);
+  }
+  // Stage c of K' is dimensions 64c .. 64c+63 of every K' row: byte 128c on.
+  // Stage c of Q' is sub-row j = 64c / D taken in reverse (query row
+  // r's + s-1-j), dimensions 64c % D on.
+  auto issue = [&](int c, uint32_t stage) {
+    const int j = (kXChunk * c) / D;
+    const int d0 = (kXChunk * c) % D;
+    const unsigned char* kb = (const unsigned char*)Kh + 128 * c;
+    const unsigned char* qb = (const unsigned char*)Qh + (int64_t)((S - 1 - j) * D + d0) * 2;
+    const uint32_t ka = lds0 + stage * kXStageBytes + (uint32_t)w * 1024;
+    const uint32_t qa = ka + kXOpBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16<0>(kb, voff_k[i], ka + i * 4096);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16<0>(qb, voff_q[i], qa + i * 4096);
+  };
+
+  // Wave (wt, wr): L^T rows (reshaped keys) 64 wt .. +63, columns (reshaped
+  // queries) 64 wr .. +63, as 2 x 2 MFMA tiles.  Operand reads: lane reads
+  // row n of a 32-row tile, inner dimensions 16 st + 8 h .. +7.
+  const int wt = w >> 1, wr = w & 1;
+  uint32_t aoff[2][4], boff[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int ra = 64 * wt + 32 * tt + n;
+      const int rb = 64 * wr + 32 * tt + n;
+      aoff[tt][st] = lds0 + (uint32_t)(ra * 128 + 16 * ((2 * st + h) ^ xswz(ra)));
+      boff[tt][st] = lds0 + kXOpBytes + (uint32_t)(rb * 128 + 16 * ((2 * st + h) ^ xswz(rb)));
+    }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) acc[tt][rr] = f32x16{};
+
+  issue(0, 0);
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t stage = (uint32_t)(c & 1) * kXStageBytes;
+    if (c + 1 < kChunks) {
+      issue(c + 1, (uint32_t)((c + 1) & 1));
+      wait_vmem<8>();   // this wave's loads of stage c are done, stage c+1 in flight
+    } else {
+      wait_vmem<0>();
+    }
+    barrier_raw();      // every wave's loads of stage c are done
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      u32x4 av[2], bv[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        av[tt] = lds_read_b128(aoff[tt][st] + stage);
+        bv[tt] = lds_read_b128(boff[tt][st] + stage);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) acc[tt][rr] = mfma32(av[tt], bv[rr], acc[tt][rr]);
+    }
+    barrier_raw();      // stage c is read by all before it is loaded again
+  }
+
+  // ---- epilogue: per (reshaped row, key block) log2-sum-exp2 ----
+  // acc[tt][rr] element v: key t' = t0 + 64 wt + 32 tt + 8 (v / 4) + 4 h + v % 4,
+  // query r' = r0 + 64 wr + 32 rr + n.  A key block is kBk consecutive t'.
+  const float c2 = a.scale_log2;
+  float* __restrict__ out = a.lse + (int64_t)bh * rq * a.nbk;
+  constexpr int kGroups = 32 / kBk;   // key blocks per 32-key MFMA tile
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = r0 + 64 * wr + 32 * rr + n;
+    const int lim = a.causal ? min(r + past, rk - 1) : rk - 1;   // last visible key
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tb = t0 + 64 * wt + 32 * tt;
+      float x[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tb + 8 * (v >> 2) + 4 * h + (v & 3);
+        x[v] = t <= lim ? acc[tt][rr][v] * c2 : -INFINITY;
+      }
+      if constexpr (kBk == 4) {
+        // 4 consecutive keys are one lane's v = 4u .. 4u+3: 4 groups per lane,
+        // group index 2u + h
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float m = fmaxf(fmaxf(x[4 * u], x[4 * u + 1]), fmaxf(x[4 * u + 2], x[4 * u + 3]));
+          float e = 0.0f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) e += fast_exp2(x[4 * u + q] - m);
+          }
+          const int kbk = tb / kBk + 2 * u + h;
+          if (r < rq && kbk < a.nbk) out[(int64_t)r * a.nbk + kbk] = e > 0.0f ? m + __log2f(e) : -INFINITY;
+        }
+      } else {
+        // kBk = 8: group v / 4; kBk = 16: group v / 8 (both lane halves share groups)
+        float mg[kGroups], eg[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          mg[g] = -INFINITY;
+          eg[g] = 0.0f;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int g = kBk == 8 ? (v >> 2) : (v >> 3);
+          mg[g] = fmaxf(mg[g], x[v]);
+        }
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) mg[g] = max_with_half_swap(mg[g]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int g = kBk == 8 ? (v >> 2) : (v >> 3);
+          if (mg[g] != -INFINITY) eg[g] += fast_exp2(x[v] - mg[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) eg[g] = sum_with_half_swap(eg[g]);
+        if (h == 0 && r < rq) {
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            const int kbk = tb / kBk + g;
+            if (kbk < a.nbk) out[(int64_t)r * a.nbk + kbk] = eg[g] > 0.0f ? mg[g] + __log2f(eg[g]) : -INFINITY;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Warp-wide (64-lane) reductions.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+constexpr int kMaxKeyBlocks = 1024;   // nbk limit of the block-sum and selection kernels
+constexpr int kColsPerLane = kMaxKeyBlocks / kWave;
+
+// One wave per (bh, query block): block sums of the reshaped softmax weights.
+template <int S>
+__global__ __launch_bounds__(kWave) void xattn_blocksum_kernel(XattnArgs a) {
+  constexpr int kBq = 64 / S;
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int qi = blockIdx.x;
+  const int rq = a.Sq / S;
+  const int past = (a.Sk - a.Sq) / S;
+  const int nbk = a.nbk;
+  const int nu = (nbk + kWave - 1) / kWave;
+  const float* __restrict__ lse = a.lse + (int64_t)bh * rq * nbk;
+  float acc[kColsPerLane];
+#pragma unroll
+  for (int u = 0; u < kColsPerLane; ++u) acc[u] = 0.0f;
+  const int rend = min(qi * kBq + kBq, rq);
+  for (int r = qi * kBq; r < rend; ++r) {
+    // key blocks this row can see at all (later ones were not written)
+    const int kb_last = a.causal ? min((r + past) / kBq, nbk - 1) : nbk - 1;
+    float v[kColsPerLane];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kColsPerLane; ++u) {
+      const int kb = u * kWave + lane;
+      v[u] = (u < nu && kb <= kb_last) ? lse[(int64_t)r * nbk + kb] : -INFINITY;
+      m = fmaxf(m, v[u]);
+    }
+    m = wave_max(m);   // finite: key 0 is visible to every row
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kColsPerLane; ++u) s += fast_exp2(v[u] - m);
+    s = wave_sum(s);
+    const float norm = m + __log2f(s);
+#pragma unroll
+    for (int u = 0; u < kColsPerLane; ++u) acc[u] += fast_exp2(v[u] - norm);
+  }
+  float* __restrict__ out = a.block_sums + ((int64_t)bh * a.nbq + qi) * nbk;
+#pragma unroll
+  for (int u = 0; u < kColsPerLane; ++u) {
+    const int kb = u * kWave + lane;
+    if (u < nu && kb < nbk) out[kb] = acc[u];
+  }
+}
+
+// One single-wave work-group per query-block row: selection by cumulative weight.
+__global__ __launch_bounds__(kWave) void mask_cumulative_kernel(const float* __restrict__ sums,
+                                                                int nbq, int nbk, float threshold,
+                                                                int keep_sink, int keep_diag,
+                                                                int causal,
+                                                                uint8_t* __restrict__ mask) {
+  __shared__ uint64_t keys[kMaxKeyBlocks];
+  __shared__ float vals[kMaxKeyBlocks];
+  __shared__ uint8_t take[kMaxKeyBlocks];
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int i = (int)(row % nbq);
+  const int diag = i + (nbk - nbq);   // query blocks are the last nbq of nbk
+  const float* __restrict__ x = sums + row * nbk;
+  uint8_t* __restrict__ out = mask + row * nbk;
+  int n2 = 1;
+  while (n2 < nbk) n2 <<= 1;
+  auto forced = [&](int c) { return (keep_sink && c == 0) || (keep_diag && c == diag); };
+  for (int c = lane; c < n2; c += kWave) {
+    if (c < nbk) {
+      const float v = x[c];
+      vals[c] = v;
+      keys[c] = rank_key(forced(c) ? 0.0f : v, c);
+    } else {
+      keys[c] = 0;   // below every real key: sorts last
+    }
+  }
+  __syncthreads();
+  // bitonic sort of keys[0 .. n2), descending
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int p = lane; p < n2; p += kWave) {
+        const int q = p ^ j;
+        if (q > p) {
+          const uint64_t kp = keys[p], kq = keys[q];
+          const bool desc = (p & k) == 0;   // this run sorts descending
+          if (desc ? (kp < kq) : (kp > kq)) {
+            keys[p] = kq;
+            keys[q] = kp;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (lane == 0) {
+    double total = 0.0;
+    for (int c = 0; c < nbk; ++c) total += (double)vals[c];
+    const double required = (double)threshold * total;
+    double before = 0.0;
+    for (int p = 0; p < nbk; ++p) {
+      const uint64_t key = keys[p];
+      take[p] = before < required ? 1 : 0;
+      before += (double)rank_key_score(key);
+    }
+  }
+  __syncthreads();
+  for (int p = lane; p < nbk; p += kWave) {
+    const int c = rank_key_column(keys[p]);
+    bool sel = take[p] != 0 || forced(c);
+    if (causal && c > diag) sel = false;
+    out[c] = sel ? 1 : 0;
+  }
+}
+
+template <int D, int S>
+hipError_t launch_xattn_ds(const XattnArgs& a, hipStream_t stream) {
+  const int rq = a.Sq / S;
+  const int nrt = (rq + kXTile - 1) / kXTile;
+  if (a.BH > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((xattn_lse_kernel<D, S>), dim3((unsigned)(nrt * a.ntc), (unsigned)a.BH),
+                     dim3(kXThreads), kXLdsBytes, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((xattn_blocksum_kernel<S>), dim3((unsigned)a.nbq, (unsigned)a.BH), dim3(kWave),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_xattn_d(const XattnArgs& a, hipStream_t stream) {
+  switch (a.stride) {
+    case 4: return launch_xattn_ds<D, 4>(a, stream);
+    case 8: return launch_xattn_ds<D, 8>(a, stream);
+    case 16: return launch_xattn_ds<D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int xattn_max_key_blocks() { return kMaxKeyBlocks; }
+
+size_t xattn_lse_bytes(int B, int H, int Sq, int Sk, int stride) {
+  const size_t nbk = (size_t)(Sk + kBlock - 1) / kBlock;
+  return (size_t)B * H * (size_t)(Sq / stride) * nbk * sizeof(float);
+}
+
+hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream) {
+  a.ntc = ((a.Sk / a.stride) + kXTile - 1) / kXTile;
+  return a.D == 64 ? launch_xattn_d<64>(a, stream) : launch_xattn_d<128>(a, stream);
+}
+
+hipError_t launch_mask_cumulative(const float* sums, int B, int H, int nbq, int nbk, float threshold,
+                                  int keep_sink, int keep_diag, int causal, uint8_t* mask,
+                                  hipStream_t stream) {
+  const int64_t rows = (int64_t)B * H * nbq;
+  hipLaunchKernelGGL(mask_cumulative_kernel, dim3((unsigned)rows), dim3(kWave), 0, stream, sums,
+                     nbq, nbk, threshold, keep_sink, keep_diag, causal, mask);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

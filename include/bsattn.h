@@ -276,6 +276,69 @@ bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache
  * current device (queries the CU count once per device). Returns 0 on error. */
 int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D);
 
+/* ------------------------------------------------------------------------ */
+/* XAttention block-importance estimator (upstream of the block mask)        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Block sums of the stride-reshaped attention estimate (XAttention guide,
+ * "algorithm flow" phases 1-2; stride-reshape section, inverse mode; the
+ * softmax + block-sum kernel description).
+ *   q : bfloat16 [B, H, Sq, D];  k : bfloat16 [B, H, Sk, D];  Sq <= Sk, the
+ *       queries being the last Sq of Sk positions
+ *   block_sums : float32 [B, H, nbq, nbk], nbq = ceil(Sq / 64), nbk = ceil(Sk / 64)
+ * With s = stride, reshaped key row t' is key rows t's .. t's+s-1 and
+ * reshaped query row r' is query rows r's+s-1 down to r's, each concatenated;
+ * the logit of (r', t') is their dot product / (sqrt(D) * s * norm); with
+ * is_causal, t' is visible to r' when t' <= r' + (Sk - Sq) / s.  Each
+ * reshaped row is softmax-normalised over its visible t', and
+ * block_sums[b, h, i, j] is the sum of those weights over the reshaped rows
+ * of query block i and the reshaped columns of key block j (64 / s each).
+ * A row of block_sums therefore adds up to the number of reshaped rows of
+ * its query block.
+ * workspace: at least bsattn_xattn_workspace_bytes(B, H, Sq, Sk, stride).
+ * Errors: NULL pointers; B, H, Sq <= 0, Sk < Sq, Sq or Sk not a multiple of
+ * stride, (Sk - Sq) % 64 != 0, norm not finite and > 0 (SHAPE); D not 64 or
+ * 128, stride not 4, 8 or 16, nbk > 1024 (UNSUPPORTED); workspace (WORKSPACE).
+ */
+size_t bsattn_xattn_workspace_bytes(int B, int H, int Sq, int Sk, int stride);
+
+bsattn_status bsattn_xattn_block_sums(const uint16_t* q, const uint16_t* k, int B, int H, int Sq,
+                                      int Sk, int D, int stride, float norm, int is_causal,
+                                      float* block_sums, void* workspace, size_t workspace_bytes,
+                                      bsattn_stream_t stream);
+
+/*
+ * Block selection by cumulative weight (XAttention guide, block-selection
+ * section).  block_sums float32 [B, H, nbq, nbk] -> mask uint8 0/1
+ * [B, H, nbq, nbk]; query block i sits at key block d = i + nbk - nbq.  Per
+ * row: total = the row's sum; required = threshold * total; column 0 (when
+ * keep_sink) and column d (when keep_diagonal) are kept and their weights set
+ * to 0; the columns are ranked by weight (ties: lower column first), and a
+ * column is kept when the weight ranked above it is below required, i.e. the
+ * shortest ranked prefix reaching required.  With is_causal, columns after d
+ * are then cleared.  Sums and the comparison are float64: the total in
+ * ascending column order, the ranked sum in rank order.
+ * Errors: NULL pointers; B, H, nbq <= 0, nbk < nbq (SHAPE); nbk > 1024
+ * (UNSUPPORTED).
+ */
+bsattn_status bsattn_build_mask_cumulative(const float* block_sums, int B, int H, int nbq, int nbk,
+                                           float threshold, int keep_sink, int keep_diagonal,
+                                           int is_causal, uint8_t* mask, bsattn_stream_t stream);
+
+/*
+ * The whole estimator (XAttention guide, "algorithm flow" phases 1-3):
+ * bsattn_xattn_block_sums, then bsattn_build_mask_cumulative on its output.
+ * block_sums may be NULL (the workspace then holds them).  The mask is the
+ * block_mask input of bsattn_fwd (Sq = Sk) or bsattn_fwd_chunk.
+ * Errors: those of the two calls.
+ */
+bsattn_status bsattn_xattn_estimate(const uint16_t* q, const uint16_t* k, int B, int H, int Sq,
+                                    int Sk, int D, int stride, float norm, float threshold,
+                                    int keep_sink, int keep_diagonal, int is_causal,
+                                    float* block_sums, uint8_t* mask, void* workspace,
+                                    size_t workspace_bytes, bsattn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

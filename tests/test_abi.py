@@ -104,6 +104,38 @@ def test_fused_fwd_validates_on_host():
     assert lib.bsattn_fwd_threshold(F, F, F, F, 0, 1, 256, 64, 0.5, 0, 1, 1, None, F, None) == 2
 
 
+def test_xattn_validates_on_host():
+    lib = _lib()
+    F = FAKE
+    ws = 1 << 40   # claimed size: no call below gets past validation
+    # block sums: q k B H Sq Sk D stride norm causal out ws ws_bytes stream
+    assert lib.bsattn_xattn_block_sums(None, F, 1, 1, 256, 256, 64, 8, 1.0, 1, F, F, ws, None) == 1
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 256, 64, 8, 1.0, 1, None, F, ws, None) == 1
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 128, 64, 8, 1.0, 1, F, F, ws, None) == 2   # Sk < Sq
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 100, 100, 64, 8, 1.0, 1, F, F, ws, None) == 2   # S % stride
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 128, 160, 64, 8, 1.0, 1, F, F, ws, None) == 2   # (Sk-Sq) % 64
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 256, 64, 8, 0.0, 1, F, F, ws, None) == 2   # norm
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 256, 64, 8, float("inf"), 1, F, F, ws, None) == 2
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 256, 96, 8, 1.0, 1, F, F, ws, None) == 3   # D
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 256, 256, 64, 2, 1.0, 1, F, F, ws, None) == 3   # stride
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 1, 64, 64 * 1025, 64, 8, 1.0, 1, F, F, ws, None) == 3
+    need = lib.bsattn_xattn_workspace_bytes(1, 2, 256, 512, 8)
+    assert need >= 2 * (256 // 8) * 8 * 4 + 2 * 4 * 8 * 4
+    assert lib.bsattn_xattn_workspace_bytes(1, 2, 256, 100, 8) == 0
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 2, 256, 512, 64, 8, 1.0, 1, F, F, need - 1, None) == 4
+    assert lib.bsattn_xattn_block_sums(F, F, 1, 2, 256, 512, 64, 8, 1.0, 1, F, None, need, None) == 4
+    # cumulative selection: sums B H nbq nbk thr sink diag causal mask stream
+    assert lib.bsattn_build_mask_cumulative(None, 1, 1, 2, 2, 0.9, 1, 1, 1, F, None) == 1
+    assert lib.bsattn_build_mask_cumulative(F, 1, 1, 2, 2, 0.9, 1, 1, 1, None, None) == 1
+    assert lib.bsattn_build_mask_cumulative(F, 1, 1, 3, 2, 0.9, 1, 1, 1, F, None) == 2
+    assert lib.bsattn_build_mask_cumulative(F, 0, 1, 2, 2, 0.9, 1, 1, 1, F, None) == 2
+    assert lib.bsattn_build_mask_cumulative(F, 1, 1, 2, 1025, 0.9, 1, 1, 1, F, None) == 3
+    # the whole estimator
+    assert lib.bsattn_xattn_estimate(F, F, 1, 1, 256, 256, 64, 8, 1.0, 0.9, 1, 1, 1, None, None, F, ws, None) == 1
+    assert lib.bsattn_xattn_estimate(F, F, 1, 1, 256, 256, 64, 4 * 3, 1.0, 0.9, 1, 1, 1, None, F, F, ws, None) == 2
+    assert lib.bsattn_xattn_estimate(F, F, 1, 1, 256, 256, 64, 8, 1.0, 0.9, 1, 1, 1, None, F, F, 16, None) == 4
+
+
 def test_chunk_fwd_validates_on_host():
     lib = _lib()
     F = FAKE
