@@ -21,8 +21,10 @@ Printed (one JSON line):
                reading a 512 MiB buffer (a read leaves no dirty lines whose
                write-back would land inside the timed call);
 * next_rows  — the mask-form and paged-KV variants of that decode (same
-               workload and flush) and a chunked prefill (the last 1024 of
-               C2's 4096 positions), each against the same roofline;
+               workload and flush), a chunked prefill (the last 1024 of
+               C2's 4096 positions), and the XAttention block estimate that
+               produces a mask upstream (C3's shape, stride 8), each against
+               its roofline;
 * cpu_baseline — the float64 CPU oracle timed on a bounded sample of the same
                workload on this host.
 
@@ -302,6 +304,55 @@ def bench_prefill_chunk(steps: int, warmup: int):
     return {"Sq": Sq, "Sk": cfg.S, "active": active, "flops": flops, "ms": ms, "cfg": cfg}
 
 
+def bench_xattn(steps: int, warmup: int):
+    """XAttention block estimate on C3's shape (B1 H32 S16384 D128, its seeded
+    q and k), stride 8, threshold 0.9, sink and diagonal kept, causal."""
+    torch = _torch()
+    import block_sparse_attention_amd as bsa
+    from block_sparse_attention_amd import inputs as gen
+
+    cfg = gen.CONFIGS["C3"]
+    qkv = gen.prefill_qkv(cfg, 0)
+    q, k = _gpu_bf16(qkv["q"]), _gpu_bf16(qkv["k"])
+    B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
+    stride, thr = 8, 0.9
+    nb = cfg.nb
+    sums = torch.empty((B, H, nb, nb), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, H, nb, nb), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(bsa.bsattn_xattn_workspace_bytes(B, H, S, S, stride), dtype=torch.uint8,
+                     device="cuda")
+    rows = S // stride
+    # reshaped GEMM flops over the causally visible reshaped pairs: 2 * (stride * D) each
+    flops = B * H * rows * (rows + 1) // 2 * 2 * stride * D
+
+    def est():
+        bsa.bsattn_xattn_estimate(q, k, stride, 1.0, thr, True, True, True, block_sums=sums,
+                                  out=mask, workspace=ws)
+
+    def timed(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    _settle(est)
+    for _ in range(warmup):
+        est()
+    ms = timed(est, steps)
+    ms_sums = timed(lambda: bsa.bsattn_xattn_block_sums(q, k, stride, 1.0, True, out=sums,
+                                                        workspace=ws), steps)
+    ms_sel = timed(lambda: bsa.bsattn_build_mask_cumulative(sums, thr, True, True, True, out=mask),
+                   steps)
+    density = float(mask.float().sum().item()) / (B * H * nb * (nb + 1) / 2)
+    return {"flops": flops, "ms": ms, "ms_sums": ms_sums, "ms_select": ms_sel,
+            "density": density, "cfg": cfg, "stride": stride, "threshold": thr}
+
+
 def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -485,6 +536,18 @@ def main(argv=None):
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "flop_per_launch": pc["flops"]}}
+        xr = bench_xattn(max(10, args.steps // 20), 3)
+        tf_all = xr["flops"] / (xr["ms"] * 1e-3) / 1e12
+        tf_sums = xr["flops"] / (xr["ms_sums"] * 1e-3) / 1e12
+        nxt["xattn_estimate"] = {
+            "workload": "XAttention block estimate on C3's shape (B1 H32 S16384 D128, seeded N(0,1) "
+                        "q, k): stride 8, threshold 0.9, sink and diagonal kept, causal",
+            "value": round(tf_all, 3), "unit": "TFLOP/s (reshaped GEMM flop / whole estimate)",
+            "ms_per_call": round(xr["ms"], 5), "ms_block_sums": round(xr["ms_sums"], 5),
+            "ms_selection": round(xr["ms_select"], 5), "mask_causal_density": round(xr["density"], 4),
+            "roofline": {"bound": "mfma", "kernel": "xattn_lse_kernel + xattn_blocksum_kernel",
+                         "achieved": round(tf_sums, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_sums / BF16_PEAK_TFLOPS, 4), "flop_per_call": xr["flops"]}}
         line["next_rows"] = nxt
 
     if not args.no_cpu:

@@ -280,68 +280,135 @@ __global__ __launch_bounds__(kWave) void xattn_blocksum_kernel(XattnArgs a) {
   }
 }
 
-// One single-wave work-group per query-block row: selection by cumulative weight.
-__global__ __launch_bounds__(kWave) void mask_cumulative_kernel(const float* __restrict__ sums,
-                                                                int nbq, int nbk, float threshold,
-                                                                int keep_sink, int keep_diag,
-                                                                int causal,
-                                                                uint8_t* __restrict__ mask) {
-  __shared__ uint64_t keys[kMaxKeyBlocks];
-  __shared__ float vals[kMaxKeyBlocks];
-  __shared__ uint8_t take[kMaxKeyBlocks];
-  const int lane = threadIdx.x;
-  const int64_t row = blockIdx.x;
+// 64-bit lane exchange with lane ^ j.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int j) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, j);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+constexpr int kSelRows = 16;   // query-block rows per selection work-group, one wave each
+
+template <int NU>
+constexpr size_t selection_lds_bytes() {
+  return (size_t)kSelRows * (kWave * NU + 1) * 4 * 2 + (size_t)kSelRows * (kWave * NU + 4);
+}
+
+// Selection by cumulative weight, kSelRows query-block rows per work-group.
+// Wave w sorts row w: its order keys (forced columns at weight 0) go through
+// a descending bitonic network over 64 * NU elements held in registers,
+// element e = NU * lane + u in key[u] (distances below NU inside a lane,
+// longer ones by lane exchange).  Then lane r of wave 0 runs row r's float64
+// sums one term at a time: the total in column order and the ranked sums in
+// rank order, from padded LDS copies of the values.  Each wave finally maps
+// its row's rank positions back to columns.
+template <int NU>
+__global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
+    const float* __restrict__ sums, int64_t rows, int nbq, int nbk, float threshold, int keep_sink,
+    int keep_diag, int causal, uint8_t* __restrict__ mask) {
+  constexpr int N = kWave * NU;
+  constexpr int LW = N + 1;   // padded row pitch (floats): lane-per-row reads hit distinct banks
+  constexpr int LT = N + 4;   // padded row pitch of the take flags (bytes)
+  extern __shared__ __attribute__((aligned(16))) unsigned char sel_smem[];
+  float* vals = (float*)sel_smem;                  // [kSelRows][LW] weights, column order
+  float* ranked = vals + kSelRows * LW;            // [kSelRows][LW] weights, rank order
+  uint8_t* take = (uint8_t*)(ranked + kSelRows * LW);   // [kSelRows][LT]
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kSelRows + w;
+  const bool valid = row < rows;
   const int i = (int)(row % nbq);
   const int diag = i + (nbk - nbq);   // query blocks are the last nbq of nbk
-  const float* __restrict__ x = sums + row * nbk;
-  uint8_t* __restrict__ out = mask + row * nbk;
-  int n2 = 1;
-  while (n2 < nbk) n2 <<= 1;
   auto forced = [&](int c) { return (keep_sink && c == 0) || (keep_diag && c == diag); };
-  for (int c = lane; c < n2; c += kWave) {
-    if (c < nbk) {
-      const float v = x[c];
-      vals[c] = v;
-      keys[c] = rank_key(forced(c) ? 0.0f : v, c);
-    } else {
-      keys[c] = 0;   // below every real key: sorts last
+
+  uint64_t key[NU];
+  if (valid) {
+    const float* __restrict__ x = sums + row * nbk;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = NU * lane + u;
+      if (c < nbk) {
+        const float v = x[c];
+        vals[w * LW + c] = v;
+        key[u] = rank_key(forced(c) ? 0.0f : v, c);
+      } else {
+        key[u] = 0;   // below every real key: sorts last
+      }
     }
-  }
-  __syncthreads();
-  // bitonic sort of keys[0 .. n2), descending
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int p = lane; p < n2; p += kWave) {
-        const int q = p ^ j;
-        if (q > p) {
-          const uint64_t kp = keys[p], kq = keys[q];
-          const bool desc = (p & k) == 0;   // this run sorts descending
-          if (desc ? (kp < kq) : (kp > kq)) {
-            keys[p] = kq;
-            keys[q] = kp;
+    // bitonic sort, descending
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        if (j < NU) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int p = u ^ j;
+            if (p > u) {
+              const bool desc = ((NU * lane + u) & k) == 0;
+              const uint64_t a = key[u], b = key[p];
+              const bool swap = desc ? (a < b) : (a > b);
+              key[u] = swap ? b : a;
+              key[p] = swap ? a : b;
+            }
+          }
+        } else {
+          const int jl = j / NU;   // lane distance
+          const bool lower = (lane & jl) == 0;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const bool desc = ((NU * lane + u) & k) == 0;
+            const uint64_t o = shfl_xor_u64(key[u], jl);
+            const bool take_other = (lower == desc) ? (o > key[u]) : (o < key[u]);
+            key[u] = take_other ? o : key[u];
           }
         }
       }
-      __syncthreads();
     }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) ranked[w * LW + NU * lane + u] = rank_key_score(key[u]);
   }
-  if (lane == 0) {
+  __syncthreads();
+  if (w == 0 && lane < kSelRows && (int64_t)blockIdx.x * kSelRows + lane < rows) {
+    const float* vr = vals + lane * LW;
+    const float* rr = ranked + lane * LW;
+    uint8_t* tr = take + lane * LT;
     double total = 0.0;
-    for (int c = 0; c < nbk; ++c) total += (double)vals[c];
+    for (int c0 = 0; c0 < nbk; c0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[q] = vr[min(c0 + q, N - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (c0 + q < nbk) total += (double)t[q];
+    }
     const double required = (double)threshold * total;
     double before = 0.0;
-    for (int p = 0; p < nbk; ++p) {
-      const uint64_t key = keys[p];
-      take[p] = before < required ? 1 : 0;
-      before += (double)rank_key_score(key);
+    for (int p0 = 0; p0 < nbk; p0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[q] = rr[min(p0 + q, N - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < nbk) {
+          tr[p0 + q] = before < required ? 1 : 0;
+          before += (double)t[q];
+        }
     }
   }
   __syncthreads();
-  for (int p = lane; p < nbk; p += kWave) {
-    const int c = rank_key_column(keys[p]);
-    bool sel = take[p] != 0 || forced(c);
-    if (causal && c > diag) sel = false;
-    out[c] = sel ? 1 : 0;
+  if (valid) {
+    uint8_t* __restrict__ out = mask + row * nbk;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e = NU * lane + u;
+      if (e < nbk) {
+        const int c = rank_key_column(key[u]);
+        bool sel = take[w * LT + e] != 0 || forced(c);
+        if (causal && c > diag) sel = false;
+        out[c] = sel ? 1 : 0;
+      }
+    }
   }
 }
 
@@ -383,13 +450,36 @@ hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream) {
   return a.D == 64 ? launch_xattn_d<64>(a, stream) : launch_xattn_d<128>(a, stream);
 }
 
+template <int NU>
+hipError_t launch_cumulative_nu(const float* sums, int64_t rows, int nbq, int nbk, float threshold,
+                                int keep_sink, int keep_diag, int causal, uint8_t* mask,
+                                hipStream_t stream) {
+  constexpr size_t lds = selection_lds_bytes<NU>();
+  auto kern = mask_cumulative_kernel<NU>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t groups = (rows + kSelRows - 1) / kSelRows;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kSelRows * kWave), lds, stream, sums, rows,
+                     nbq, nbk, threshold, keep_sink, keep_diag, causal, mask);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_cumulative(const float* sums, int B, int H, int nbq, int nbk, float threshold,
                                   int keep_sink, int keep_diag, int causal, uint8_t* mask,
                                   hipStream_t stream) {
   const int64_t rows = (int64_t)B * H * nbq;
-  hipLaunchKernelGGL(mask_cumulative_kernel, dim3((unsigned)rows), dim3(kWave), 0, stream, sums,
-                     nbq, nbk, threshold, keep_sink, keep_diag, causal, mask);
-  return hipGetLastError();
+  if (nbk <= 64)
+    return launch_cumulative_nu<1>(sums, rows, nbq, nbk, threshold, keep_sink, keep_diag, causal, mask, stream);
+  if (nbk <= 128)
+    return launch_cumulative_nu<2>(sums, rows, nbq, nbk, threshold, keep_sink, keep_diag, causal, mask, stream);
+  if (nbk <= 256)
+    return launch_cumulative_nu<4>(sums, rows, nbq, nbk, threshold, keep_sink, keep_diag, causal, mask, stream);
+  if (nbk <= 512)
+    return launch_cumulative_nu<8>(sums, rows, nbq, nbk, threshold, keep_sink, keep_diag, causal, mask, stream);
+  return launch_cumulative_nu<16>(sums, rows, nbq, nbk, threshold, keep_sink, keep_diag, causal, mask, stream);
 }
 
 }  // namespace bsattn
