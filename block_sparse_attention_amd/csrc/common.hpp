@@ -92,6 +92,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same, and every LDS operation of this wave has completed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_lds0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ void barrier_raw() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

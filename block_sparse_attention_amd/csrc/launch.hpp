@@ -78,7 +78,7 @@ struct XattnArgs {
   float scale_log2;     // log2(e) / (sqrt(D) * stride * norm)
   int BH, Sq, Sk, D, stride, nbq, nbk;
   int causal;
-  int ntc;              // set by the launcher: 128-wide reshaped column tiles
+  int ntc, nrt;         // set by the launcher: 128-wide reshaped column / row tiles
 };
 hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream);
 hipError_t launch_mask_cumulative(const float* sums, int B, int H, int nbq, int nbk, float threshold,

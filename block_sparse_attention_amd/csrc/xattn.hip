@@ -46,13 +46,14 @@ constexpr int kXChunk = 64;           // inner dimensions per LDS stage
 constexpr int kXOpBytes = kXTile * kXChunk * 2;   // one operand tile per stage: 16 KiB
 constexpr int kXStageBytes = 2 * kXOpBytes;       // K' then Q'
 constexpr int kXLdsBytes = 2 * kXStageBytes;      // two stages
+constexpr int kXBand = 8;             // row tiles walked together (L2 reuse)
 
 // 16-byte granule g of LDS row r (128 bytes) is stored at granule g ^ xswz(r):
 // the 32-row, 16-byte-per-lane operand reads then touch every bank once.
 __device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
 
-// Grid (row tiles x column tiles, B*H).  A tile whose columns all lie past
-// the causal limit of every row it holds is not computed.
+// One work-group per (head, row tile, column tile).  A tile whose columns all
+// lie past the causal limit of every row it holds is not computed.
 template <int D, int S>
 __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
   constexpr int kChunks = S * D / kXChunk;   // inner-dimension stages
@@ -66,10 +67,31 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
   const int h = lane >> 5;
   const int n = lane & 31;
 
-  const int bh = blockIdx.y;
-  const int ntc = a.ntc;
-  const int rt = blockIdx.x / ntc;
-  const int ct = blockIdx.x - rt * ntc;
+  // Tile order: work-group L runs on XCD L % 8.  When B*H is a multiple of
+  // 8, XCD x takes heads x, x+8, ...; within a head it walks bands of
+  // kXBand row tiles, column tile by column tile, so the ~64 tiles resident
+  // on one XCD share kXBand query strips and as many key strips in its L2.
+  const int ntc = a.ntc, nrt = a.nrt;
+  int bh, rt, ct;
+  {
+    const int L = blockIdx.x;
+    const int per_head = nrt * ntc;
+    int idx;
+    if ((a.BH & 7) == 0) {
+      const int k = L >> 3;
+      bh = (L & 7) + 8 * (k / per_head);
+      idx = k % per_head;
+    } else {
+      bh = L / per_head;
+      idx = L % per_head;
+    }
+    const int band_tiles = kXBand * ntc;
+    const int band = idx / band_tiles;
+    const int rem = idx - band * band_tiles;
+    const int rows_in_band = min(kXBand, nrt - band * kXBand);
+    ct = rem / rows_in_band;
+    rt = band * kXBand + (rem - ct * rows_in_band);
+  }
   const int rq = a.Sq / S, rk = a.Sk / S;          // reshaped lengths
   const int past = (a.Sk - a.Sq) / S;             // reshaped causal offset
   const int r0 = rt * kXTile, t0 = ct * kXTile;
@@ -131,27 +153,31 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
   issue(0, 0);
   for (int c = 0; c < kChunks; ++c) {
     const uint32_t stage = (uint32_t)(c & 1) * kXStageBytes;
-    if (c + 1 < kChunks) {
-      issue(c + 1, (uint32_t)((c + 1) & 1));
-      wait_vmem<8>();   // this wave's loads of stage c are done, stage c+1 in flight
-    } else {
-      wait_vmem<0>();
-    }
-    barrier_raw();      // every wave's loads of stage c are done
+    // This wave's loads of stage c are done and its reads of stage c-1 have
+    // returned; after the barrier every wave is there, so stage c is in LDS
+    // and the slot of stage c-1 is free for stage c+1, which then has the
+    // whole of this stage's MFMA work to arrive.
+    wait_vmem_lds0<0>();
+    barrier_raw();
+    if (c + 1 < kChunks) issue(c + 1, (uint32_t)((c + 1) & 1));
+    // all 16 operand reads of the stage first, into distinct registers, so the
+    // MFMAs wait on them progressively instead of on each read in turn
+    u32x4 av[4][2], bv[4][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      u32x4 av[2], bv[2];
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        av[tt] = lds_read_b128(aoff[tt][st] + stage);
-        bv[tt] = lds_read_b128(boff[tt][st] + stage);
+        av[st][tt] = lds_read_b128(aoff[tt][st] + stage);
+        bv[st][tt] = lds_read_b128(boff[tt][st] + stage);
       }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) acc[tt][rr] = mfma32(av[tt], bv[rr], acc[tt][rr]);
-    }
-    barrier_raw();      // stage c is read by all before it is loaded again
+        for (int rr = 0; rr < 2; ++rr) acc[tt][rr] = mfma32(av[st][tt], bv[st][rr], acc[tt][rr]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: per (reshaped row, key block) log2-sum-exp2 ----
@@ -414,11 +440,10 @@ __global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
 
 template <int D, int S>
 hipError_t launch_xattn_ds(const XattnArgs& a, hipStream_t stream) {
-  const int rq = a.Sq / S;
-  const int nrt = (rq + kXTile - 1) / kXTile;
-  if (a.BH > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((xattn_lse_kernel<D, S>), dim3((unsigned)(nrt * a.ntc), (unsigned)a.BH),
-                     dim3(kXThreads), kXLdsBytes, stream, a);
+  const int64_t tiles = (int64_t)a.BH * a.nrt * a.ntc;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((xattn_lse_kernel<D, S>), dim3((unsigned)tiles), dim3(kXThreads), kXLdsBytes,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((xattn_blocksum_kernel<S>), dim3((unsigned)a.nbq, (unsigned)a.BH), dim3(kWave),
@@ -447,6 +472,7 @@ size_t xattn_lse_bytes(int B, int H, int Sq, int Sk, int stride) {
 
 hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream) {
   a.ntc = ((a.Sk / a.stride) + kXTile - 1) / kXTile;
+  a.nrt = ((a.Sq / a.stride) + kXTile - 1) / kXTile;
   return a.D == 64 ? launch_xattn_d<64>(a, stream) : launch_xattn_d<128>(a, stream);
 }
 
