@@ -57,6 +57,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
     "prefill": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "prefill.hip"),
     "decode": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "decode.hip"),
+    "xattn": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "xattn.hip"),
 }
 
 
@@ -418,6 +419,8 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg (profiling runs)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the mask-form / paged decode and chunked-prefill measurements")
+    ap.add_argument("--xattn-only", action="store_true",
+                    help="only run the XAttention estimate leg (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 10 times (counter calibration)")
     args = ap.parse_args(argv)
@@ -442,6 +445,12 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "launches": 10}), flush=True)
+        return 0
+
+    if args.xattn_only:
+        xr = bench_xattn(max(10, args.steps // 20), 3)
+        print(json.dumps({"xattn_ms": xr["ms"], "block_sums_ms": xr["ms_sums"],
+                          "selection_ms": xr["ms_select"]}), flush=True)
         return 0
 
     if args.no_prefill:
@@ -547,7 +556,8 @@ def main(argv=None):
             "ms_selection": round(xr["ms_select"], 5), "mask_causal_density": round(xr["density"], 4),
             "roofline": {"bound": "mfma", "kernel": "xattn_lse_kernel + xattn_blocksum_kernel",
                          "achieved": round(tf_sums, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf_sums / BF16_PEAK_TFLOPS, 4), "flop_per_call": xr["flops"]}}
+                         "frac": round(tf_sums / BF16_PEAK_TFLOPS, 4), "flop_per_call": xr["flops"],
+                         "traffic": _traffic("xattn", "C3")}}
         line["next_rows"] = nxt
 
     if not args.no_cpu:
