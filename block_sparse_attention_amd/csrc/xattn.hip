@@ -46,7 +46,10 @@ constexpr int kXChunk = 64;           // inner dimensions per LDS stage
 constexpr int kXOpBytes = kXTile * kXChunk * 2;   // one operand tile per stage: 16 KiB
 constexpr int kXStageBytes = 2 * kXOpBytes;       // K' then Q'
 constexpr int kXLdsBytes = 2 * kXStageBytes;      // two stages
-constexpr int kXBand = 8;             // row tiles walked together (L2 reuse)
+#ifndef BSATTN_XBAND
+#define BSATTN_XBAND 8
+#endif
+constexpr int kXBand = BSATTN_XBAND;  // row tiles walked together (L2 reuse)
 
 // 16-byte granule g of LDS row r (128 bytes) is stored at granule g ^ xswz(r):
 // the 32-row, 16-byte-per-lane operand reads then touch every bank once.
