@@ -85,7 +85,7 @@ __device__ __forceinline__ int swz_k(int r) {
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return D == 64 ? (r & 2) : ((r & 3) << 1);
+  return D == 64 ? ((r & 2) << 1) : ((r & 3) << 2);
 }
 
 
