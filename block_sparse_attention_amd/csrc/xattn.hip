@@ -186,68 +186,88 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
   // ---- epilogue: per (reshaped row, key block) log2-sum-exp2 ----
   // acc[tt][rr] element v: key t' = t0 + 64 wt + 32 tt + 8 (v / 4) + 4 h + v % 4,
   // query r' = r0 + 64 wr + 32 rr + n.  A key block is kBk consecutive t'.
+  // The scale is applied inside the exponent's fma (max of the raw sums, then
+  // 2^(c acc - c max)); only a wave whose keys are not all visible to all its
+  // rows (on the causal diagonal, or past the end of K) tests each key.
   const float c2 = a.scale_log2;
   float* __restrict__ out = a.lse + (int64_t)bh * rq * a.nbk;
   constexpr int kGroups = 32 / kBk;   // key blocks per 32-key MFMA tile
+  const int wt0 = t0 + 64 * wt, wr0 = r0 + 64 * wr;
+  const bool wave_masked = (wt0 + 63 > rk - 1) || (a.causal && wt0 + 63 > wr0 + past);
+  auto epilogue = [&](auto masked_c) {
+    constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = r0 + 64 * wr + 32 * rr + n;
-    const int lim = a.causal ? min(r + past, rk - 1) : rk - 1;   // last visible key
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = wr0 + 32 * rr + n;
+      const int lim = a.causal ? min(r + past, rk - 1) : rk - 1;   // last visible key
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tb = t0 + 64 * wt + 32 * tt;
-      float x[16];
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tb = wt0 + 32 * tt;
+        float x[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = tb + 8 * (v >> 2) + 4 * h + (v & 3);
-        x[v] = t <= lim ? acc[tt][rr][v] * c2 : -INFINITY;
-      }
-      if constexpr (kBk == 4) {
-        // 4 consecutive keys are one lane's v = 4u .. 4u+3: 4 groups per lane,
-        // group index 2u + h
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float m = fmaxf(fmaxf(x[4 * u], x[4 * u + 1]), fmaxf(x[4 * u + 2], x[4 * u + 3]));
-          float e = 0.0f;
-          if (m != -INFINITY) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) e += fast_exp2(x[4 * u + q] - m);
+        for (int v = 0; v < 16; ++v) {
+          x[v] = acc[tt][rr][v];
+          if constexpr (kMasked) {
+            const int t = tb + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (t > lim) x[v] = -INFINITY;
           }
-          const int kbk = tb / kBk + 2 * u + h;
-          if (r < rq && kbk < a.nbk) out[(int64_t)r * a.nbk + kbk] = e > 0.0f ? m + __log2f(e) : -INFINITY;
         }
-      } else {
-        // kBk = 8: group v / 4; kBk = 16: group v / 8 (both lane halves share groups)
-        float mg[kGroups], eg[kGroups];
+        if constexpr (kBk == 4) {
+          // 4 consecutive keys are one lane's v = 4u .. 4u+3: 4 groups per lane,
+          // group index 2u + h
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          mg[g] = -INFINITY;
-          eg[g] = 0.0f;
-        }
+          for (int u = 0; u < 4; ++u) {
+            const float m = fmaxf(fmaxf(x[4 * u], x[4 * u + 1]), fmaxf(x[4 * u + 2], x[4 * u + 3]));
+            const float mc = m * c2;
+            float e = 0.0f;
+            if (!kMasked || m != -INFINITY) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int g = kBk == 8 ? (v >> 2) : (v >> 3);
-          mg[g] = fmaxf(mg[g], x[v]);
-        }
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) mg[g] = max_with_half_swap(mg[g]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int g = kBk == 8 ? (v >> 2) : (v >> 3);
-          if (mg[g] != -INFINITY) eg[g] += fast_exp2(x[v] - mg[g]);
-        }
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) eg[g] = sum_with_half_swap(eg[g]);
-        if (h == 0 && r < rq) {
+              for (int q = 0; q < 4; ++q) e += fast_exp2(fmaf(x[4 * u + q], c2, -mc));
+            }
+            const int kbk = tb / kBk + 2 * u + h;
+            if (r < rq && kbk < a.nbk)
+              out[(int64_t)r * a.nbk + kbk] = e > 0.0f ? mc + __log2f(e) : -INFINITY;
+          }
+        } else {
+          // kBk = 8: group v / 4; kBk = 16: group v / 8 (both lane halves share groups)
+          float mg[kGroups], eg[kGroups];
 #pragma unroll
           for (int g = 0; g < kGroups; ++g) {
-            const int kbk = tb / kBk + g;
-            if (kbk < a.nbk) out[(int64_t)r * a.nbk + kbk] = eg[g] > 0.0f ? mg[g] + __log2f(eg[g]) : -INFINITY;
+            mg[g] = -INFINITY;
+            eg[g] = 0.0f;
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int g = kBk == 8 ? (v >> 2) : (v >> 3);
+            mg[g] = fmaxf(mg[g], x[v]);
+          }
+          float mcg[kGroups];
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            mg[g] = max_with_half_swap(mg[g]);
+            mcg[g] = mg[g] * c2;
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int g = kBk == 8 ? (v >> 2) : (v >> 3);
+            if (!kMasked || mg[g] != -INFINITY) eg[g] += fast_exp2(fmaf(x[v], c2, -mcg[g]));
+          }
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) eg[g] = sum_with_half_swap(eg[g]);
+          if (h == 0 && r < rq) {
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+              const int kbk = tb / kBk + g;
+              if (kbk < a.nbk)
+                out[(int64_t)r * a.nbk + kbk] = eg[g] > 0.0f ? mcg[g] + __log2f(eg[g]) : -INFINITY;
+            }
           }
         }
       }
     }
-  }
+  };
+  if (wave_masked) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // Warp-wide (64-lane) reductions.
