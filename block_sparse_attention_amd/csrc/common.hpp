@@ -72,6 +72,42 @@ __device__ __forceinline__ int rank_key_column(uint64_t key) {
   return (int)(0xffffffffu - (uint32_t)key);
 }
 
+// Top-k cut over a wave by a bitwise radix select.  key[u] holds the order
+// key of column 64 u + lane (distinct keys; 0 for padding, below every real
+// key); chunks u >= nch are not read.  On return the selected columns are
+// exactly those with (key & hm) >= prefix: walking the key bits from the top,
+// the prefix of the topk-th largest key is fixed one bit at a time from
+// ballot counts, stopping as soon as the keys on the prefix are exactly the
+// ones still needed.  Requires 0 < topk < number of real keys.
+template <int NCH>
+__device__ __forceinline__ void wave_topk_cut(const uint64_t (&key)[NCH], int nch, int topk,
+                                              uint64_t& hm, uint64_t& prefix) {
+  int want = topk;
+  prefix = 0;
+  hm = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t m = ~0ull << bit;
+    const uint64_t target = prefix | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+      if (u < nch) cnt += __popcll(wave_ballot((key[u] & m) == target));
+    int cand;
+    if (cnt >= want) {
+      prefix = target;
+      cand = cnt;
+    } else {
+      want -= cnt;
+      cand = 0;
+#pragma unroll
+      for (int u = 0; u < NCH; ++u)
+        if (u < nch) cand += __popcll(wave_ballot((key[u] & m) == prefix));
+    }
+    hm = m;
+    if (cand == want) break;
+  }
+}
+
 // ---- wave-level memory and matrix-core primitives ----
 
 // One wave-wide 16-byte-per-lane load straight into LDS: lane l reads

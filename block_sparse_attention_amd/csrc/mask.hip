@@ -75,45 +75,44 @@ __global__ __launch_bounds__(kTopkThreads) void mask_topk_kernel(const float* __
 constexpr int kWaveRows = 4;        // rows per work-group, one wave each
 constexpr int kWaveMaxNb = 1024;    // rows up to this length use the one-wave kernel
 
-// One wave per score row: the row's order keys sit in LDS; lane owns columns
-// lane, lane+64, ... and counts the keys above each of its own.
+// One wave per score row: the row's order keys sit in registers, lane l
+// holding columns l, l+64, ... (NCH chunks of 64), and a radix select over
+// the wave (wave_topk_cut) finds the top-k cut.
+template <int NCH>
 __global__ __launch_bounds__(kWaveRows * kWave) void mask_topk_wave_kernel(
     const float* __restrict__ scores, int64_t rows, int nb, int topk, int dense2, int diag,
     uint8_t* __restrict__ mask) {
-  __shared__ uint64_t keys[kWaveRows][kWaveMaxNb];
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int64_t row = (int64_t)blockIdx.x * kWaveRows + w;
-  if (row >= rows) return;  // the whole wave leaves; only wave-level syncs below
+  if (row >= rows) return;  // the whole wave leaves; only wave-level operations below
   const int i = (int)(row % nb);
   const float* x = scores + row * (int64_t)nb;
   uint8_t* out = mask + row * (int64_t)nb;
+  const int nch = (nb + kWave - 1) / kWave;
 
   const bool dense_row = dense2 && i >= nb - 2;
-  if (dense_row || topk >= nb || topk == 0) {
-    const bool all = dense_row || topk >= nb;
-    for (int j = lane; j < nb; j += kWave) out[j] = ((j <= i) && (all || (diag && j == i))) ? 1 : 0;
-    return;
-  }
-  uint64_t* kr = keys[w];
-  for (int c = lane; c < nb; c += kWave) kr[c] = rank_key(x[c], c);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (int j0 = 0; j0 < nb; j0 += kWave) {
-    const int j = j0 + lane;
-    if (j0 > i) {            // the whole group lies above the diagonal
-      if (j < nb) out[j] = 0;
-      continue;
+  const bool all = dense_row || topk >= nb;
+  const bool ranked = !all && topk > 0;
+  uint64_t key[NCH];
+  uint64_t hm = 0, prefix = 0;
+  if (ranked) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = kWave * u + lane;
+      key[u] = c < nb ? rank_key(x[c], c) : 0ull;   // 0 is below every real key
     }
-    const uint64_t kj = (j < nb) ? kr[j] : ~0ull;
-    int beat = 0;
-    for (int c = 0; c < nb; ++c) beat += kr[c] > kj;
-    if (j < nb) {
+    wave_topk_cut(key, nch, topk, hm, prefix);
+  }
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int j = kWave * u + lane;
+    if (u < nch && j < nb) {
       bool pick;
-      if (j > i) pick = false;
-      else if (diag && j == i) pick = true;
-      else pick = beat < topk;
+      if (j > i) pick = false;                 // tril
+      else if (diag && j == i) pick = true;    // forced diagonal
+      else if (all) pick = true;
+      else pick = ranked && (key[u] & hm) >= prefix;
       out[j] = pick ? 1 : 0;
     }
   }
@@ -168,8 +167,16 @@ hipError_t launch_mask_topk(const float* scores, int B, int H, int nb, int topk,
   const int64_t rows = (int64_t)B * H * nb;
   if (nb <= kWaveMaxNb) {
     const int64_t blocks = (rows + kWaveRows - 1) / kWaveRows;
-    hipLaunchKernelGGL(mask_topk_wave_kernel, dim3((unsigned)blocks), dim3(kWaveRows * kWave), 0,
-                       stream, scores, rows, nb, topk, dense2, diag, mask);
+    const dim3 grid((unsigned)blocks), block(kWaveRows * kWave);
+#define BSATTN_TOPK(NCH)                                                                           \
+  hipLaunchKernelGGL(mask_topk_wave_kernel<NCH>, grid, block, 0, stream, scores, rows, nb, topk, \
+                     dense2, diag, mask)
+    if (nb <= 64) BSATTN_TOPK(1);
+    else if (nb <= 128) BSATTN_TOPK(2);
+    else if (nb <= 256) BSATTN_TOPK(4);
+    else if (nb <= 512) BSATTN_TOPK(8);
+    else BSATTN_TOPK(16);
+#undef BSATTN_TOPK
   } else {
     hipLaunchKernelGGL(mask_topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), 0, stream,
                        scores, nb, topk, dense2, diag, mask);

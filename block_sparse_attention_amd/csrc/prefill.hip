@@ -234,13 +234,9 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       const bool all = dense_row || (SRC == kSrcTopk && a.topk >= nbk);
       const bool none = SRC == kSrcTopk && a.topk == 0 && !dense_row;
       const bool ranked = SRC == kSrcTopk && !all && !none;
-      // Top-k by a bitwise radix select over the wave: the row's order keys
-      // (distinct: ties are broken by the column) sit in registers, lane l
-      // holding columns l, l+64, ...; walking the key bits from the top, the
-      // prefix of the topk-th largest key is fixed one bit at a time from
-      // ballot counts, stopping as soon as the keys matching the prefix are
-      // exactly the ones still needed.  A column is selected when its key,
-      // cut to the decided bits, is at least that prefix.
+      // Top-k by a bitwise radix select over the wave (wave_topk_cut): the
+      // row's order keys (distinct: ties are broken by the column) sit in
+      // registers, lane l holding columns l, l+64, ...
       uint64_t key[kMaxKeyChunks];
       uint64_t hm = 0, prefix = 0;
       if (ranked) {
@@ -249,28 +245,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
           const int c = 64 * u + lane;
           key[u] = c < nbk ? rank_key(x[c], c) : 0ull;   // 0 is below every real key
         }
-        int want = a.topk;
-        for (int bit = 63; bit >= 0; --bit) {
-          const uint64_t m = ~0ull << bit;
-          const uint64_t target = prefix | (1ull << bit);
-          int cnt = 0;
-#pragma unroll
-          for (int u = 0; u < kMaxKeyChunks; ++u)
-            if (64 * u < nbk) cnt += __popcll(wave_ballot((key[u] & m) == target));
-          int cand;
-          if (cnt >= want) {
-            prefix = target;
-            cand = cnt;
-          } else {
-            want -= cnt;
-            cand = 0;
-#pragma unroll
-            for (int u = 0; u < kMaxKeyChunks; ++u)
-              if (64 * u < nbk) cand += __popcll(wave_ballot((key[u] & m) == prefix));
-          }
-          hm = m;
-          if (cand == want) break;
-        }
+        wave_topk_cut(key, (nbk + kWave - 1) / kWave, a.topk, hm, prefix);
       }
 #pragma unroll
       for (int u = 0; u < kMaxKeyChunks; ++u) {
