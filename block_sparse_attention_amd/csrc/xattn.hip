@@ -40,16 +40,29 @@ namespace bsattn {
 
 namespace {
 
-constexpr int kXTile = 128;           // reshaped rows and columns per tile
-constexpr int kXThreads = 256;        // 4 waves, each 64 x 64 of the tile
+// A tile is 64 WT reshaped keys x 128 reshaped queries, computed by 2 WT waves
+// of 64 x 64 each.
+constexpr int kXTileR = 128;          // reshaped queries (rows of L) per tile
 constexpr int kXChunk = 64;           // inner dimensions per LDS stage
-constexpr int kXOpBytes = kXTile * kXChunk * 2;   // one operand tile per stage: 16 KiB
-constexpr int kXStageBytes = 2 * kXOpBytes;       // K' then Q'
-constexpr int kXLdsBytes = 2 * kXStageBytes;      // two stages
+template <int WT>
+struct XTile {
+  static constexpr int kWaves = 2 * WT;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kT = 64 * WT;                       // reshaped keys per tile
+  static constexpr int kOpBytesK = kT * kXChunk * 2;       // K' part of a stage
+  static constexpr int kStageBytes = (kT + kXTileR) * kXChunk * 2;
+  static constexpr int kLdsBytes = 2 * kStageBytes;        // two stages
+};
+template <int WT>
+constexpr int kXThreadsFor = 2 * WT * kWave;
 #ifndef BSATTN_XBAND
 #define BSATTN_XBAND 8
 #endif
 constexpr int kXBand = BSATTN_XBAND;  // row tiles walked together (L2 reuse)
+#ifndef BSATTN_XWT
+#define BSATTN_XWT 2
+#endif
+constexpr int kXWT = BSATTN_XWT;      // waves along the reshaped keys (tile: 64 kXWT keys)
 
 // 16-byte granule g of LDS row r (128 bytes) is stored at granule g ^ xswz(r):
 // the 32-row, 16-byte-per-lane operand reads then touch every bank once.
@@ -57,8 +70,9 @@ __device__ __forceinline__ int xswz(int r) { return (r >> 1) & 7; }
 
 // One work-group per (head, row tile, column tile).  A tile whose columns all
 // lie past the causal limit of every row it holds is not computed.
-template <int D, int S>
-__global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
+template <int D, int S, int WT>
+__global__ __launch_bounds__(kXThreadsFor<WT>) void xattn_lse_kernel(XattnArgs a) {
+  using T = XTile<WT>;
   constexpr int kChunks = S * D / kXChunk;   // inner-dimension stages
   constexpr int kBk = 64 / S;                // reshaped columns per 64-token key block
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -97,23 +111,30 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
   }
   const int rq = a.Sq / S, rk = a.Sk / S;          // reshaped lengths
   const int past = (a.Sk - a.Sq) / S;             // reshaped causal offset
-  const int r0 = rt * kXTile, t0 = ct * kXTile;
-  if (a.causal && t0 > r0 + kXTile - 1 + past) return;   // the whole tile is masked
+  const int r0 = rt * kXTileR, t0 = ct * T::kT;
+  if (a.causal && t0 > r0 + kXTileR - 1 + past) return;   // the whole tile is masked
 
   const uint16_t* __restrict__ Kh = a.k + (int64_t)bh * a.Sk * D;
   const uint16_t* __restrict__ Qh = a.q + (int64_t)bh * a.Sq * D;
 
-  // DMA: instruction kk (0..15) of an operand tile covers its rows 8kk .. 8kk+7;
-  // lane l fills LDS granule l % 8 of row 8kk + l / 8 with the source granule
-  // that the swizzle puts there.  Wave w issues kk = w, w+4, w+8, w+12.
-  uint32_t voff_k[4], voff_q[4];
+  // DMA: instruction kk of an operand tile covers its rows 8kk .. 8kk+7; lane
+  // l fills LDS granule l % 8 of row 8kk + l / 8 with the source granule that
+  // the swizzle puts there.  Wave w issues kk = w, w + 2 WT, ...: kIK of the
+  // K' tile's T::kT / 8 and kIQ of the Q' tile's 16.
+  constexpr int kIK = T::kT / 8 / T::kWaves, kIQ = kXTileR / 8 / T::kWaves;
+  uint32_t voff_k[kIK], voff_q[kIQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (w + 4 * i) + (lane >> 3);
+  for (int i = 0; i < kIK; ++i) {
+    const int row = 8 * (w + T::kWaves * i) + (lane >> 3);
     const int g = (lane & 7) ^ xswz(row);
     const int kr = min(t0 + row, rk - 1);   // rows past the end re-read the last (masked later)
-    const int qr = min(r0 + row, rq - 1);   // rows past the end are never stored
     voff_k[i] = (uint32_t)(((int64_t)kr * S * D + 8 * g) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < kIQ; ++i) {
+    const int row = 8 * (w + T::kWaves * i) + (lane >> 3);
+    const int g = (lane & 7) ^ xswz(row);
+    const int qr = min(r0 + row, rq - 1);   // rows past the end are never stored
     voff_q[i] = (uint32_t)(((int64_t)qr * S * D + 8 * g) * 2);
   }
   // Stage c of K' is dimensions 64c .. 64c+63 of every K' row: byte 128c on.
@@ -124,12 +145,12 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
     const int d0 = (kXChunk * c) % D;
     const unsigned char* kb = (const unsigned char*)Kh + 128 * c;
     const unsigned char* qb = (const unsigned char*)Qh + (int64_t)((S - 1 - j) * D + d0) * 2;
-    const uint32_t ka = lds0 + stage * kXStageBytes + (uint32_t)w * 1024;
-    const uint32_t qa = ka + kXOpBytes;
+    const uint32_t ka = lds0 + stage * T::kStageBytes + (uint32_t)w * 1024;
+    const uint32_t qa = ka + T::kOpBytesK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16<0>(kb, voff_k[i], ka + i * 4096);
+    for (int i = 0; i < kIK; ++i) dma16<0>(kb, voff_k[i], ka + i * T::kWaves * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16<0>(qb, voff_q[i], qa + i * 4096);
+    for (int i = 0; i < kIQ; ++i) dma16<0>(qb, voff_q[i], qa + i * T::kWaves * 1024);
   };
 
   // Wave (wt, wr): L^T rows (reshaped keys) 64 wt .. +63, columns (reshaped
@@ -144,7 +165,7 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
       const int ra = 64 * wt + 32 * tt + n;
       const int rb = 64 * wr + 32 * tt + n;
       aoff[tt][st] = lds0 + (uint32_t)(ra * 128 + 16 * ((2 * st + h) ^ xswz(ra)));
-      boff[tt][st] = lds0 + kXOpBytes + (uint32_t)(rb * 128 + 16 * ((2 * st + h) ^ xswz(rb)));
+      boff[tt][st] = lds0 + T::kOpBytesK + (uint32_t)(rb * 128 + 16 * ((2 * st + h) ^ xswz(rb)));
     }
 
   f32x16 acc[2][2];
@@ -155,7 +176,7 @@ __global__ __launch_bounds__(kXThreads) void xattn_lse_kernel(XattnArgs a) {
 
   issue(0, 0);
   for (int c = 0; c < kChunks; ++c) {
-    const uint32_t stage = (uint32_t)(c & 1) * kXStageBytes;
+    const uint32_t stage = (uint32_t)(c & 1) * T::kStageBytes;
     // This wave's loads of stage c are done and its reads of stage c-1 have
     // returned; after the barrier every wave is there, so stage c is in LDS
     // and the slot of stage c-1 is free for stage c+1, which then has the
@@ -465,8 +486,14 @@ template <int D, int S>
 hipError_t launch_xattn_ds(const XattnArgs& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)a.BH * a.nrt * a.ntc;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((xattn_lse_kernel<D, S>), dim3((unsigned)tiles), dim3(kXThreads), kXLdsBytes,
-                     stream, a);
+  using T = XTile<kXWT>;
+  auto kern = xattn_lse_kernel<D, S, kXWT>;
+  if (T::kLdsBytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(T::kThreads), T::kLdsBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((xattn_blocksum_kernel<S>), dim3((unsigned)a.nbq, (unsigned)a.BH), dim3(kWave),
@@ -494,8 +521,8 @@ size_t xattn_lse_bytes(int B, int H, int Sq, int Sk, int stride) {
 }
 
 hipError_t launch_xattn_block_sums(XattnArgs a, hipStream_t stream) {
-  a.ntc = ((a.Sk / a.stride) + kXTile - 1) / kXTile;
-  a.nrt = ((a.Sq / a.stride) + kXTile - 1) / kXTile;
+  a.ntc = ((a.Sk / a.stride) + XTile<kXWT>::kT - 1) / XTile<kXWT>::kT;
+  a.nrt = ((a.Sq / a.stride) + kXTileR - 1) / kXTileR;
   return a.D == 64 ? launch_xattn_d<64>(a, stream) : launch_xattn_d<128>(a, stream);
 }
 
