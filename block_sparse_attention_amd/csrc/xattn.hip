@@ -15,7 +15,8 @@
 // Three kernels:
 // * xattn_lse_kernel: one 128 x 128 tile of L^T per work-group (4 waves, each
 //   64 x 64 from 32x32x16 bf16 MFMAs; operands stream HBM -> LDS by direct
-//   loads, double-buffered over 64-dimension chunks).  The tile's epilogue
+//   loads, double-buffered over 64-dimension chunks; tiles ordered so the
+//   ones resident on an XCD share operand strips in its L2).  The tile's epilogue
 //   reduces every (reshaped row, 64-token key block) to the log2-sum-exp2 of
 //   its scaled logits and stores it.  Tiles are independent: the row softmax
 //   needs the whole row, and per-block log-sums let the next kernel normalise
@@ -28,7 +29,7 @@
 //   diagonal kept, the rest ranked by weight and kept while the weight
 //   ranked above is below threshold * total.  Sums are float64, the total in
 //   ascending column order and the ranked sum in rank order, one term at a
-//   time; the ranking is a bitonic sort of order keys in LDS.
+//   time; the ranking is a bitonic sort of order keys held in registers.
 #include <math.h>
 
 #include <type_traits>
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kXThreadsFor<WT>) void xattn_lse_kernel(XattnArgs a
   else epilogue(std::false_type{});
 }
 
-// Warp-wide (64-lane) reductions.
+// Wave-wide (64-lane) reductions.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -304,12 +305,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 constexpr int kMaxKeyBlocks = 1024;   // nbk limit of the block-sum and selection kernels
-constexpr int kColsPerLane = kMaxKeyBlocks / kWave;
 
 // One wave per (bh, query block): block sums of the reshaped softmax weights.
-template <int S>
+// Lane l handles key blocks l, l+64, ... (NU of them, 64 NU >= nbk).
+template <int S, int NU>
 __global__ __launch_bounds__(kWave) void xattn_blocksum_kernel(XattnArgs a) {
   constexpr int kBq = 64 / S;
+  constexpr int kColsPerLane = NU;
   const int lane = threadIdx.x;
   const int bh = blockIdx.y;
   const int qi = blockIdx.x;
@@ -496,8 +498,12 @@ hipError_t launch_xattn_ds(const XattnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(T::kThreads), T::kLdsBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((xattn_blocksum_kernel<S>), dim3((unsigned)a.nbq, (unsigned)a.BH), dim3(kWave),
-                     0, stream, a);
+  const dim3 grid((unsigned)a.nbq, (unsigned)a.BH);
+  if (a.nbk <= 64) hipLaunchKernelGGL((xattn_blocksum_kernel<S, 1>), grid, dim3(kWave), 0, stream, a);
+  else if (a.nbk <= 128) hipLaunchKernelGGL((xattn_blocksum_kernel<S, 2>), grid, dim3(kWave), 0, stream, a);
+  else if (a.nbk <= 256) hipLaunchKernelGGL((xattn_blocksum_kernel<S, 4>), grid, dim3(kWave), 0, stream, a);
+  else if (a.nbk <= 512) hipLaunchKernelGGL((xattn_blocksum_kernel<S, 8>), grid, dim3(kWave), 0, stream, a);
+  else hipLaunchKernelGGL((xattn_blocksum_kernel<S, 16>), grid, dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
