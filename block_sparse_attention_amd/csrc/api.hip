@@ -152,6 +152,10 @@ static bsattn_status fwd_common(PrefillArgs a, int B, int H, int Sq, int Sk, int
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
   a.nbq = nblocks(Sq); a.nbk = nblocks(Sk);
   a.causal = is_causal ? 1 : 0;
+  // D = 64: four waves per item when the items are no more than one round of
+  // resident work-groups (four per CU), two otherwise
+  const long long items = (long long)B * H * a.nbq;
+  a.ks = (D == 64 && items <= 4LL * device_cu_count()) ? 2 : 1;
   return launch_prefill(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
 }
 

@@ -38,6 +38,7 @@ struct PrefillArgs {
   int src;               // PrefillSource
   int B, H, Sq, Sk, D, nbq, nbk;   // Sq <= Sk: the queries are the last Sq positions
   int causal;
+  int ks;                // D = 64: key splits per work item, 1 or 2 (D = 128 always uses 2)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // LDS one forward work-group needs (K/V ring plus a block list of nbk entries).

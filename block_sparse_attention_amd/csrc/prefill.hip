@@ -43,6 +43,8 @@
 //   K/V stay in that XCD's L2.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -678,21 +680,18 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   }
 }
 
-// Key splits per work item by head dim: at D = 64 two waves (all keys each)
-// keep the per-item overhead lowest; at D = 128 four waves (half the keys
-// each) halve the per-wave registers, so two waves fit per SIMD.
-#ifndef BSATTN_KS64
-#define BSATTN_KS64 1
-#endif
+// Key splits per work item.  At D = 128 always four waves (half the keys
+// each): that halves the per-wave registers, so two waves fit per SIMD.  At
+// D = 64 the caller chooses (PrefillArgs::ks): two waves over all keys have
+// the lowest per-item overhead and win when the items fill the GPU; four waves
+// per item put twice the waves on the GPU when items are few (one round of
+// resident work-groups or less).
 #ifndef BSATTN_KS128
 #define BSATTN_KS128 2
 #endif
-template <int D>
-constexpr int kKeySplits = D == 64 ? BSATTN_KS64 : BSATTN_KS128;
 
-template <int D, bool CAUSAL, int SRC>
+template <int D, int KS, bool CAUSAL, int SRC>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int KS = kKeySplits<D>;
   const int BH = a.B * a.H;
   int mode = 0, group = 1;
   if (BH % 8 == 0) {
@@ -720,22 +719,28 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t prefill_lds_bytes(int D, int nbk) {
-  return D == 64 ? lds_bytes<64, kKeySplits<64>>(nbk) : lds_bytes<128, kKeySplits<128>>(nbk);
+  return D == 64 ? std::max(lds_bytes<64, 1>(nbk), lds_bytes<64, 2>(nbk))
+                 : lds_bytes<128, BSATTN_KS128>(nbk);
 }
 
-template <int D, bool CAUSAL>
+template <int D, int KS, bool CAUSAL>
 hipError_t launch_src(const PrefillArgs& a, hipStream_t stream) {
   switch (a.src) {
-    case kSrcList: return launch_t<D, CAUSAL, kSrcList>(a, stream);
-    case kSrcTopk: return launch_t<D, CAUSAL, kSrcTopk>(a, stream);
-    case kSrcThreshold: return launch_t<D, CAUSAL, kSrcThreshold>(a, stream);
-    default: return launch_t<D, CAUSAL, kSrcMask>(a, stream);
+    case kSrcList: return launch_t<D, KS, CAUSAL, kSrcList>(a, stream);
+    case kSrcTopk: return launch_t<D, KS, CAUSAL, kSrcTopk>(a, stream);
+    case kSrcThreshold: return launch_t<D, KS, CAUSAL, kSrcThreshold>(a, stream);
+    default: return launch_t<D, KS, CAUSAL, kSrcMask>(a, stream);
   }
 }
 
+template <int D, int KS>
+hipError_t launch_ks(const PrefillArgs& a, hipStream_t stream) {
+  return a.causal ? launch_src<D, KS, true>(a, stream) : launch_src<D, KS, false>(a, stream);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.D == 64) return a.causal ? launch_src<64, true>(a, stream) : launch_src<64, false>(a, stream);
-  return a.causal ? launch_src<128, true>(a, stream) : launch_src<128, false>(a, stream);
+  if (a.D == 64) return a.ks == 2 ? launch_ks<64, 2>(a, stream) : launch_ks<64, 1>(a, stream);
+  return launch_ks<128, BSATTN_KS128>(a, stream);
 }
 
 }  // namespace bsattn

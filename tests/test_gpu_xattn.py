@@ -179,3 +179,13 @@ def test_full_size_sampled_heads():
     # every head: rows add up to 8 reshaped rows, nothing after the diagonal
     np.testing.assert_allclose(sums.sum(axis=-1), 8.0, rtol=1e-5)
     assert not np.triu(mask, 1).any()
+
+
+def test_deterministic():
+    q, k = _qk(1, 4, 1024, 1024, 128, 21)
+    qg, kg = to_gpu_bf16(q), to_gpu_bf16(k)
+    say("[xattn-estimate] determinism")
+    m1, s1 = bsa.bsattn_xattn_estimate(qg, kg, 8, 1.0, 0.9, True, True, True, write_sums=True)
+    m2, s2 = bsa.bsattn_xattn_estimate(qg, kg, 8, 1.0, 0.9, True, True, True, write_sums=True)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(m1, m2)
