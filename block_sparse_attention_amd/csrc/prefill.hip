@@ -186,6 +186,18 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     return (CAUSAL && j * 64 + 63 > q0 + past) || (j * 64 + 64 > Sk);
   };
 
+  // The mask row's first 256 bytes are requested before Q, so the list can be
+  // built (and the first K/V tiles requested) while Q is still on its way.
+  // (Unconditional loads at a clamped column keep the compiler from waiting
+  // on each; columns past lim are ignored when the list is built.)
+  uint8_t mpre[kMaxKeyChunks];
+  if constexpr (SRC == kSrcMask) {
+    const uint8_t* mrow = a.mask + ((int64_t)bh * nbq + i) * nbk;
+#pragma unroll
+    for (int u = 0; u < kMaxKeyChunks; ++u) mpre[u] = mrow[min(kWave * u + lane, lim - 1)];
+    asm volatile("" ::: "memory");   // issued before the Q loads below
+  }
+
   // Q^T as the B operand of S^T = K . Q^T: lane holds row qrow, dims 16s + 8h .. +8.
   u32x4 qf[C::kSteps];
   {
@@ -221,7 +233,16 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       }
     } else if constexpr (SRC == kSrcMask) {
       const uint8_t* mrow = a.mask + ((int64_t)bh * nbq + i) * nbk;
-      for (int c0 = 0; c0 < lim; c0 += kWave) {
+#pragma unroll
+      for (int u = 0; u < kMaxKeyChunks; ++u) {
+        if (kWave * u >= lim) break;
+        const int j = kWave * u + lane;
+        const bool ok = j < lim && mpre[u] != 0;
+        const uint64_t bits = wave_ballot(ok);
+        if (ok) list[count + __popcll(bits & below)] = (uint16_t)j;
+        count += __popcll(bits);
+      }
+      for (int c0 = kWave * kMaxKeyChunks; c0 < lim; c0 += kWave) {   // rows past 256 blocks
         const int j = c0 + lane;
         const bool ok = j < lim && mrow[j] != 0;
         const uint64_t bits = wave_ballot(ok);
