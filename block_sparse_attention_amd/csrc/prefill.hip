@@ -190,11 +190,18 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // built (and the first K/V tiles requested) while Q is still on its way.
   // (Unconditional loads at a clamped column keep the compiler from waiting
   // on each; columns past lim are ignored when the list is built.)
+  // The fused forms do the same with the block-score row (nb <= 256).
   uint8_t mpre[kMaxKeyChunks];
+  float xpre[kMaxKeyChunks];
   if constexpr (SRC == kSrcMask) {
     const uint8_t* mrow = a.mask + ((int64_t)bh * nbq + i) * nbk;
 #pragma unroll
     for (int u = 0; u < kMaxKeyChunks; ++u) mpre[u] = mrow[min(kWave * u + lane, lim - 1)];
+    asm volatile("" ::: "memory");   // issued before the Q loads below
+  } else if constexpr (SRC == kSrcTopk || SRC == kSrcThreshold) {
+    const float* xrow = a.scores + ((int64_t)bh * nbk + i) * nbk;
+#pragma unroll
+    for (int u = 0; u < kMaxKeyChunks; ++u) xpre[u] = xrow[min(kWave * u + lane, nbk - 1)];
     asm volatile("" ::: "memory");   // issued before the Q loads below
   }
 
@@ -250,9 +257,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         count += __popcll(bits);
       }
     } else {
-      // square problem: nbq = nbk = nb
-      const int64_t row = (int64_t)bh * nbk + i;
-      const float* x = a.scores + row * nbk;
+      // square problem: nbq = nbk = nb; the score row is in xpre (loaded above)
       const bool dense_row = a.dense2 && i >= nbk - 2;
       const bool all = dense_row || (SRC == kSrcTopk && a.topk >= nbk);
       const bool none = SRC == kSrcTopk && a.topk == 0 && !dense_row;
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 #pragma unroll
         for (int u = 0; u < kMaxKeyChunks; ++u) {
           const int c = 64 * u + lane;
-          key[u] = c < nbk ? rank_key(x[c], c) : 0ull;   // 0 is below every real key
+          key[u] = c < nbk ? rank_key(xpre[u], c) : 0ull;   // 0 is below every real key
         }
         wave_topk_cut(key, (nbk + kWave - 1) / kWave, a.topk, hm, prefix);
       }
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         bool sel = false;
         if (j < nbk && j <= i) {   // tril: columns above the diagonal are never selected
           if (all) sel = true;
-          else if (SRC == kSrcThreshold) sel = dense_row || x[j] > a.threshold;
+          else if (SRC == kSrcThreshold) sel = dense_row || xpre[u] > a.threshold;
           else if (ranked) sel = (key[u] & hm) >= prefix;
           if (a.diag && j == i) sel = true;
         }
