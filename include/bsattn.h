@@ -297,9 +297,10 @@ int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks
  * A row of block_sums therefore adds up to the number of reshaped rows of
  * its query block.
  * workspace: at least bsattn_xattn_workspace_bytes(B, H, Sq, Sk, stride).
- * Errors: NULL pointers; B, H, Sq <= 0, Sk < Sq, Sq or Sk not a multiple of
- * stride, (Sk - Sq) % 64 != 0, norm not finite and > 0 (SHAPE); D not 64 or
- * 128, stride not 4, 8 or 16, nbk > 1024 (UNSUPPORTED); workspace (WORKSPACE).
+ * Errors: NULL pointers; B, H, Sq <= 0, B * H > 65535, Sk < Sq, Sq or Sk not
+ * a multiple of stride, (Sk - Sq) % 64 != 0, norm not finite and > 0 (SHAPE);
+ * D not 64 or 128, stride not 4, 8 or 16, nbk > 1024 (UNSUPPORTED);
+ * workspace missing or smaller than bsattn_xattn_workspace_bytes (WORKSPACE).
  */
 size_t bsattn_xattn_workspace_bytes(int B, int H, int Sq, int Sk, int stride);
 
