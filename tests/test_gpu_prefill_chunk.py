@@ -56,6 +56,27 @@ def test_chunk_dense_and_empty_rows(D):
     assert (got[0, 1, 64:128] == 0).all()
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sk", [16384, 16448, 20000])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_long_rows(Sk, D, causal):
+    """Mask rows of 256, 257 and 313 key blocks (the list walks up to four
+    64-column words; longer rows take another path): a few columns scattered
+    over the row, some rows whose only columns lie in the last words."""
+    Sq = 192
+    q, k, v, m = _case(1, 2, Sq, Sk, D, Sk + D + causal, density=0.03)
+    nbk = m.shape[-1]
+    m[0, 0, 0, :] = 0
+    m[0, 0, 0, [63, 64, 191, 192, nbk - 1]] = 1        # word edges and the last column
+    m[0, 1, 1, :] = 0
+    m[0, 1, 1, nbk - 3:] = 1                           # only the row's last columns
+    m[0, 1, 2, :] = 0
+    m[0, 1, 2, [0, 255]] = 1
+    say(f"[prefill-chunk] long rows Sq={Sq} Sk={Sk} nbk={nbk} D={D} causal={causal} blocks={int(m.sum())}")
+    check_close(_gpu(q, k, v, m, causal), _oracle(q, k, v, m, causal),
+                f"chunk long rows Sk{Sk} D{D} c{causal}")
+
+
 def test_square_chunk_is_the_square_forward_bitwise():
     cfg = gen.CONFIGS["C1"]
     inp = gen.prefill_inputs(cfg, 0)
