@@ -21,8 +21,9 @@
 // * software pipeline per wave: the next selected block's K loads are issued
 //   right after the current block's S^T, its V loads right after the current
 //   block's P.V, so a block's loads are in flight during the previous block's
-//   softmax and P.V.  Rows past the sequence end are clamped to its last row
-//   (no branches around loads) and masked in the scores.
+//   softmax and P.V.  Loads go through a buffer resource bounded to the
+//   block's valid rows, so rows past the sequence end read as zero (no
+//   branches around loads); their scores are masked.
 #include <math.h>
 
 #include "common.hpp"

@@ -10,12 +10,14 @@
 //
 // How it is mapped to CDNA4 (this is not the guide's kernel design):
 // * Two or four wave64s per work item.  Waves w and w^1 take query rows
-//   0..31 and 32..63.  With two waves (D = 64) each sees all 64 keys of a
-//   block; with four (D = 128) wave w also takes keys 32 (w >> 1) .. +31 only,
-//   the two key halves run as independent online softmaxes and are merged
-//   once per item through LDS.  Splitting the keys halves the per-wave
-//   registers (two waves per SIMD at D = 128 instead of one) without reading
-//   the K/V tiles from LDS more than once per query row.
+//   0..31 and 32..63.  With two waves (KS = 1: D = 64 when the items fill
+//   the GPU) each sees all 64 keys of a block; with four (KS = 2: always at
+//   D = 128, and at D = 64 when the items fit in one round of resident
+//   work-groups) wave w also takes keys 32 (w >> 1) .. +31 only, the two key
+//   halves run as independent online softmaxes and are merged once per item
+//   through LDS.  Splitting the keys halves the per-wave registers (two waves
+//   per SIMD at D = 128 instead of one) without reading the K/V tiles from
+//   LDS more than once per query row.
 // * Scores are formed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16:
 //   the accumulator gives each lane ONE query row (lane % 32) and 16 of the
 //   wave's 32 keys, so the row max / row sum are in-lane reductions plus a
