@@ -92,6 +92,21 @@ struct VTile {
   u32x4 f[DCfg<D>::kVPer];
 };
 
+// Position of the r-th (from 0) set bit of x; x has more than r set bits.
+__device__ __forceinline__ int nth_set_bit(uint64_t x, int r) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(x & ((1ull << w) - 1));
+    if (r >= c) {
+      r -= c;
+      x >>= w;
+      pos += w;
+    }
+  }
+  return pos;
+}
+
 // A selected block: its index in the sequence, and for the paged cache its physical page.
 struct BlockRef {
   int blk;
@@ -127,23 +142,50 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int nbb = (len + 63) / 64;
   const int ratio = MODE == kDecodePaged ? a.page_size / 64 : 1;   // 64-token blocks per page
 
-  // this split's slot range; this wave takes slots my_start + w + kWaves * j
   const int nslots = a.max_sel;
-  const int bps = nslots / ns;
-  const int rem = nslots % ns;
-  // Index forms: a contiguous range of the (compact, -1 padded) list.  Mask
-  // form: every ns-th column starting at sid, so the selected blocks of a
-  // row spread evenly over the splits wherever they sit in the row.
-  const bool strided = MODE == kDecodeMask;
-  const int my_len = strided ? (nslots - sid + ns - 1) / ns : bps + (sid < rem ? 1 : 0);
-  const int my_start = strided ? sid : bps * sid + min(sid, rem);
-  const int slot_step = strided ? ns : 1;
+  const int64_t sel_row = ((int64_t)b * a.Hkv + kvh) * nslots;
+
+  // Index forms: this split takes a contiguous range of the (compact, -1
+  // padded) list, and wave w its slots my_start + w + kWaves j.
+  // Mask form: the row's selected blocks are ranked by column; this split
+  // takes ranks my_start .. my_start + my_len - 1 and wave w ranks
+  // my_start + w + kWaves j, so every split and every wave gets an even share
+  // of the selected blocks wherever they sit in the row.  The row's
+  // selection is read kMaskBatch columns at a time as lane-uniform words.
+  constexpr int kMaskWords = 8;
+  constexpr int kMaskBatch = kMaskWords * kWave;
+  uint64_t mw[kMaskWords] = {};
+  auto mask_words = [&](int q0) {
+    uint8_t mb[kMaskWords];
+#pragma unroll
+    for (int u = 0; u < kMaskWords; ++u)   // unconditional, clamped: all loads in flight at once
+      mb[u] = a.block_mask[sel_row + min(q0 + kWave * u + lane, nslots - 1)];
+#pragma unroll
+    for (int u = 0; u < kMaskWords; ++u) {
+      const int j = q0 + kWave * u + lane;
+      mw[u] = wave_ballot(j < nslots && j < nbb && mb[u] != 0);
+    }
+  };
+  int my_len, my_start;
+  if constexpr (MODE == kDecodeMask) {
+    int nsel = 0;
+    for (int q0 = 0; q0 < nslots; q0 += kMaskBatch) {
+      mask_words(q0);
+#pragma unroll
+      for (int u = 0; u < kMaskWords; ++u) nsel += __popcll(mw[u]);
+    }
+    const int per = nsel / ns, extra = nsel % ns;
+    my_len = per + (sid < extra ? 1 : 0);
+    my_start = per * sid + min(sid, extra);
+  } else {
+    const int bps = nslots / ns, rem = nslots % ns;
+    my_len = bps + (sid < rem ? 1 : 0);
+    my_start = bps * sid + min(sid, rem);
+  }
   const int nper = my_len > w ? (my_len - w + kWaves - 1) / kWaves : 0;
 
   const uint32_t rsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
-
-  const int64_t sel_row = ((int64_t)b * a.Hkv + kvh) * nslots;
 
   // Q^T as the B operand: column col = query head kvh*G + col (zero when col >= G).
   u32x4 qf[C::kSteps];
@@ -281,12 +323,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   };
 
   for (int c0 = 0; c0 < nper; c0 += kWave) {
-    // this wave's next 64 slots: lane j holds slot my_start + slot_step * (w + kWaves * (c0 + j))
+    // this wave's next 64 slots: lane j holds slot (index forms) or rank
+    // (mask form) my_start + w + kWaves * (c0 + j)
     int bv = -1;
-    if (c0 + lane < nper) {
-      const int slot = my_start + slot_step * (w + kWaves * (c0 + lane));
-      if constexpr (MODE == kDecodeMask) bv = a.block_mask[sel_row + slot] ? slot : -1;
-      else bv = a.block_indices[sel_row + slot];
+    const bool want = c0 + lane < nper;
+    const int slot = my_start + w + kWaves * (c0 + lane);
+    if constexpr (MODE == kDecodeMask) {
+      // the column of rank `slot`: walk the row's words, counting selections
+      int seen = 0;
+      for (int q0 = 0; q0 < nslots; q0 += kMaskBatch) {
+        if (nslots > kMaskBatch) mask_words(q0);   // one batch stays from the count
+#pragma unroll
+        for (int u = 0; u < kMaskWords; ++u) {
+          const int pc = __popcll(mw[u]);
+          const int r = slot - seen;
+          if (want && r >= 0 && r < pc) bv = q0 + kWave * u + nth_set_bit(mw[u], r);
+          seen += pc;
+        }
+      }
+    } else if (want) {
+      bv = a.block_indices[sel_row + slot];
     }
     bool ok = bv >= 0 && bv < nbb;
     int pg = 0;
