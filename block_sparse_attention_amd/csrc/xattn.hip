@@ -404,7 +404,8 @@ __global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
         vals[w * LW + c] = v;
         key[u] = rank_key(forced(c) ? 0.0f : v, c);
       } else {
-        key[u] = 0;   // below every real key: sorts last
+        vals[w * LW + c] = 0.0f;   // the total's groups of 8 may reach past nbk
+        key[u] = 0;                // below every real key: sorts last
       }
     }
     // bitonic sort, descending
@@ -445,27 +446,33 @@ __global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
     const float* vr = vals + lane * LW;
     const float* rr = ranked + lane * LW;
     uint8_t* tr = take + lane * LT;
+    // Columns in groups of 8; the columns past nbk hold +0.0, which leaves
+    // the sum (and every comparison with it) as it was.
     double total = 0.0;
     for (int c0 = 0; c0 < nbk; c0 += 8) {
       float t[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) t[q] = vr[min(c0 + q, N - 1)];
+      for (int q = 0; q < 8; ++q) t[q] = vr[c0 + q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (c0 + q < nbk) total += (double)t[q];
+      for (int q = 0; q < 8; ++q) total += (double)t[q];
     }
     const double required = (double)threshold * total;
+    // Ranks in groups of 8 without per-rank branches: ranks past nbk hold the
+    // padding keys (sorted last), so their flags and the sum after them are
+    // never read.  N is a multiple of 8, so a group never leaves the row.
     double before = 0.0;
     for (int p0 = 0; p0 < nbk; p0 += 8) {
       float t[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) t[q] = rr[min(p0 + q, N - 1)];
+      for (int q = 0; q < 8; ++q) t[q] = rr[p0 + q];
+      uint32_t f[2] = {0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (p0 + q < nbk) {
-          tr[p0 + q] = before < required ? 1 : 0;
-          before += (double)t[q];
-        }
+      for (int q = 0; q < 8; ++q) {
+        f[q >> 2] |= (before < required ? 1u : 0u) << (8 * (q & 3));
+        before += (double)t[q];
+      }
+      *(uint32_t*)(tr + p0) = f[0];
+      *(uint32_t*)(tr + p0 + 4) = f[1];
     }
   }
   __syncthreads();
