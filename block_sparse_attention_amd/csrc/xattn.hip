@@ -420,7 +420,9 @@ __global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
             if (p > u) {
               const bool desc = ((NU * lane + u) & k) == 0;
               const uint64_t a = key[u], b = key[p];
-              const bool swap = desc ? (a < b) : (a > b);
+              // keys are distinct apart from the padding zeros, whose order
+              // does not matter: one comparison decides either direction
+              const bool swap = (a < b) == desc;
               key[u] = swap ? b : a;
               key[p] = swap ? a : b;
             }
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(kSelRows * kWave) void mask_cumulative_kernel(
           for (int u = 0; u < NU; ++u) {
             const bool desc = ((NU * lane + u) & k) == 0;
             const uint64_t o = shfl_xor_u64(key[u], jl);
-            const bool take_other = (lower == desc) ? (o > key[u]) : (o < key[u]);
+            const bool take_other = (o > key[u]) == (lower == desc);
             key[u] = take_other ? o : key[u];
           }
         }
