@@ -426,8 +426,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(sharding over several GPUs is described, not implemented)", file=sys.stderr)
         return 2
 
     torch = _torch()
