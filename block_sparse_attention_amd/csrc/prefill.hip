@@ -484,6 +484,9 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // Iteration t: wait + barrier (K_{t+1}, V_{t-1} landed; every wave is done
   // with K_t and V_{t-2}); load V_t and K_{t+2}; then
   //   P.V of block t-1 | Q.K^T of block t+1 | exp of block t.
+  // In the iteration with no K_{t+2} to load, the last block's V tile goes
+  // into that free K slot instead, one iteration early, so the last block
+  // does not wait for its own V load.
   Sc sa, sb;
   Pr pa, pb;
   if (nblk > 0) {
@@ -523,6 +526,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     barrier_raw();
     issue(vt, IsV{}, jt);
     if (t + 2 < nblk) issue(kt, IsK{}, list[t + 2]);
+    else issue(kt, IsV{}, list[t + 1]);   // the last block's V, into the K slot nothing needs
     if (needs_mask(jt)) mask_block(jt, s_cur);
 
     u32x4 op[kSlots];
@@ -580,17 +584,16 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     l += rs;
   };
   // The last iteration, t = nblk - 1 >= 1 (block t may need masking).
-  auto last = [&](auto vt, auto vp, int t, Sc& s_cur, const Pr& p_prev, Pr& p_cur) {
+  // Its V tile was loaded one iteration ahead into the K slot that no K
+  // tile needed any more (kv_c), so the wait at the top covers it.
+  auto last = [&](auto kv_c, auto vp, int t, Sc& s_cur, const Pr& p_prev, Pr& p_cur) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[t]);
     wait_vmem<0>();
     barrier_raw();
-    issue(vt, IsV{}, list[t]);
     pv(vp, p_prev);
     if (needs_mask(j)) mask_block(j, s_cur);
     softmax(s_cur, p_cur);
-    wait_vmem<0>();
-    barrier_raw();
-    pv(vt, p_cur);
+    pv(kv_c, p_cur);
   };
 
   if (nblk > 1) {
@@ -598,6 +601,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     wait_vmem<0>();
     barrier_raw();
     if (2 < nblk) issue(K0{}, IsK{}, list[2]);
+    else issue(K0{}, IsV{}, list[1]);     // nblk = 2: block 1's V into the free K slot
     qk(K1{}, sb);
     const int j0 = __builtin_amdgcn_readfirstlane((int)list[0]);
     if (needs_mask(j0)) mask_block(j0, sa);
@@ -612,8 +616,9 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       ++t;
     }
     // t == nblk - 1: its scores are in sb when t is odd, in sa when even
-    if (t & 1) last(V1{}, V0{}, t, sb, pa, pb);
-    else last(V0{}, V1{}, t, sa, pb, pa);
+    // block t's V sits in K slot (t + 1) & 1
+    if (t & 1) last(K0{}, V0{}, t, sb, pa, pb);
+    else last(K1{}, V1{}, t, sa, pb, pa);
   } else if (nblk == 1) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[0]);
     if (needs_mask(j)) mask_block(j, sa);
@@ -626,9 +631,9 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // ---- merge the two key halves of each row group, normalise and store ----
   // Wave (rg, kh) finishes O^T tiles kh*kDT/2 .. +kDT/2-1 of its rows; it
   // hands the other half of its tiles to its partner (rg, 1-kh) through the
-  // K slots of the ring (free: every wave passed a barrier after its last
-  // Q.K^T, and no K load is in flight) and its row max / row sum through
-  // `stats`.
+  // K slots of the ring (free once every wave is past its last P.V, which may
+  // read the last block's V tile from a K slot; no load is in flight) and its
+  // row max / row sum through `stats`.
   if constexpr (KS == 1) {
     // one wave holds the whole row: normalise and store
     const float lt = sum_with_half_swap(l);
@@ -655,6 +660,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) xout[(t * 16 + ii) * kWave + lane] = o[(1 - KH) * kHalf + t][ii];
   };
+  __syncthreads();   // the last block's V tile, read from a K slot, is done with
   if (kh == 0) hand_over(std::integral_constant<int, 0>{});
   else hand_over(std::integral_constant<int, 1>{});
   stats[w * 2 * kWave + lane] = m;
