@@ -163,3 +163,48 @@ def test_c2_gpu_mask_drives_the_forward_pass():
     mask = om.build_mask_topk(inp["scores"], cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
     x = _f64(inp)
     check_close(out, oa.prefill(x["q"], x["k"], x["v"], mask, True), "C1 end to end")
+
+
+@pytest.mark.parametrize("B,H,D", [(1, 2, 64), (2, 72, 64), (1, 2, 128)])
+@pytest.mark.parametrize("dense", [True, False])
+def test_rising_scores_take_the_rescale_path(B, H, D, dense):
+    """Scores shifted up block by block (one query dimension is a constant,
+    the same key dimension grows with the key block), so each later block's
+    scores exceed the exponent offset of the blocks before it by more than
+    the 2^8 partial-sum margin: the forward's raise-and-redo step runs in the
+    pipelined iterations and in the last block.  Within a block the scores
+    keep their N(0, 1) spread.  Two heads at D = 64 run with four waves per
+    item, 72 heads (1152 items) with two; D = 128."""
+    S = 512
+    nb = S // 64
+    rng = np.random.default_rng(1000 * D + H + dense)
+    qf = rng.standard_normal((B, H, S, D), dtype=np.float32)
+    kf = rng.standard_normal((B, H, S, D), dtype=np.float32)
+    qf[..., D - 1] = 4.0
+    kf[..., D - 1] = np.repeat(np.arange(nb, dtype=np.float32) * (150.0 if D == 64 else 250.0), 64)
+    q, k = gen.f32_to_bf16_bits(qf), gen.f32_to_bf16_bits(kf)
+    # Rows early in a diagonal block attend to one or two keys, so their
+    # outputs are single values of V: V ~ N(0, 1/16) keeps those near 1, where
+    # the bfloat16 rounding of the output itself stays well inside the
+    # tolerance (at |o| >= 4 a half unit in the last place is 0.0156).
+    v = gen.f32_to_bf16_bits(0.25 * rng.standard_normal((B, H, S, D), dtype=np.float32))
+    if dense:
+        mask = np.ones((B, H, nb, nb), np.uint8)
+    else:
+        mask = (rng.random((B, H, nb, nb)) < 0.6).astype(np.uint8)
+        mask[..., np.arange(nb), np.arange(nb)] = 1
+    x = {n: gen.bf16_bits_to_f64(a) for n, a in (("q", q), ("k", k), ("v", v))}
+    # the data does what the test is for: in every row with two or more
+    # blocks, each block's maximum exceeds the previous block's by more than
+    # 8 / c (the margin of the lazy exponent offset)
+    c = np.log2(np.e) / np.sqrt(D)
+    s = (x["q"][0, 0] @ x["k"][0, 0].T) / np.sqrt(D)
+    for r in range(64, S):
+        i = r // 64
+        sel = [j for j in range(i + 1) if mask[0, 0, i, j]]
+        mx = [s[r, 64 * j:min(64 * j + 64, r + 1)].max() for j in sel]
+        assert all((b - a) * c > 10 for a, b in zip(mx, mx[1:])), (r, mx)
+    say(f"[prefill] rising scores B{B} H{H} D{D} dense={dense}")
+    got = _run_gpu({"q": q, "k": k, "v": v}, mask, True)
+    want = oa.prefill(x["q"], x["k"], x["v"], mask, True)
+    check_close(got, want, f"rising scores B{B} H{H} D{D}")
