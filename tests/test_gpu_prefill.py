@@ -208,3 +208,10 @@ def test_rising_scores_take_the_rescale_path(B, H, D, dense):
     got = _run_gpu({"q": q, "k": k, "v": v}, mask, True)
     want = oa.prefill(x["q"], x["k"], x["v"], mask, True)
     check_close(got, want, f"rising scores B{B} H{H} D{D}")
+    if dense:
+        # the fused form (row selection in the forward's prologue) runs the
+        # same redo: top-k with k = nb keeps every causal block
+        say(f"[prefill] rising scores, fused top-k, B{B} H{H} D{D}")
+        fused = bsa.bsattn_fwd_topk(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
+                                    to_gpu(np.zeros((B, H, nb, nb), np.float32)), nb)
+        check_close(gpu_bf16_to_f64(fused), want, f"rising scores fused B{B} H{H} D{D}")
