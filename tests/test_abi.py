@@ -210,3 +210,47 @@ def test_binding_refuses_host_tensors():
         bsa.bsattn_fwd(q, q, q, m)
     with pytest.raises(ValueError, match="GPU"):
         bsa.bsattn_build_mask_topk(torch.zeros((1, 1, 2, 2)), 1)
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "bsattn.h"
+
+/* A C99 caller of the ABI: every call below fails validation on the host,
+   so no device memory is needed; the split heuristic is plain host code. */
+int main(void) {
+  const uint16_t* f16 = (const uint16_t*)0x1000;   /* never dereferenced */
+  const float* f32 = (const float*)0x1000;
+  uint8_t* m8 = (uint8_t*)0x1000;
+  int bad = 0;
+  bad += bsattn_build_mask_topk(NULL, 1, 1, 4, 2, 0, 1, m8, NULL) != BSATTN_ERR_NULL;
+  bad += bsattn_build_mask_topk(f32, 1, 1, 4, 5, 0, 1, m8, NULL) != BSATTN_ERR_SHAPE;
+  bad += bsattn_fwd(f16, f16, f16, m8, 1, 1, 64, 96, 1, (uint16_t*)f16, NULL, 0, NULL)
+         != BSATTN_ERR_UNSUPPORTED;
+  bad += bsattn_decode_num_splits(8, 32, 8, 64, 128, 256) != 4;
+  printf("%s %s %d\n", bsattn_version(), bsattn_status_string(BSATTN_ERR_SHAPE), bad);
+  return bad;
+}
+"""
+
+
+def test_c_program_compiles_links_and_calls_the_abi(tmp_path):
+    """The header is plain C99 and the library links and runs from C."""
+    import shutil
+    import subprocess
+    _lib()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    exe = tmp_path / "caller"
+    src.write_text(C_PROGRAM)
+    libdir = os.path.dirname(bsa.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), f"-L{libdir}", "-l:libbsattn.so",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.stdout, r.stderr)
+    words = r.stdout.split()
+    assert words[0] == bsa.bsattn_version() and words[-1] == "0", r.stdout
