@@ -233,9 +233,10 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
  *                ignored).
  * Everything else (q, k, v, cu_seqlens_k, out, the split count, workspace,
  * GQA head mapping, the merge) is as in bsattn_decode_gqa, with num_blocks
- * in the place of max_selected_blocks, except that the mask's columns are
- * dealt to the splits round-robin (split s takes columns s, s + num_splits,
- * ...), which spreads a row's selected blocks evenly over the splits.
+ * in the place of max_selected_blocks, except that the split count divides
+ * the row's selected blocks, taken in column order, into even shares (split
+ * s takes ranks [s*n/num_splits, (s+1)*n/num_splits) up to rounding, n the
+ * row's selected count), so the work is even wherever the selected columns sit.
  * Errors as bsattn_decode_gqa (num_blocks <= 0 or num_splits > num_blocks:
  * SHAPE).
  */
