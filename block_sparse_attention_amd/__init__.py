@@ -214,7 +214,7 @@ def bsattn_fwd(q, k, v, block_mask, is_causal: bool = True, out=None, workspace=
     _dev(out, "out", torch.bfloat16, 4)
     need = bsattn_fwd_workspace_bytes(B, H, S, D)
     ws_ptr, ws_bytes = 0, 0
-    if need:
+    if need and (is_causal or workspace is not None):
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()

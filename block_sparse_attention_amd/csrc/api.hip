@@ -134,8 +134,9 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
 }
 
 size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
-  (void)B; (void)H; (void)S; (void)D;
-  return 0;
+  if (B <= 0 || H <= 0 || S <= 0 || !head_dim_ok(D)) return 0;
+  if ((long long)B * H * nblocks(S) > 0x7fffffffLL) return 0;
+  return split_layout(B, H, nblocks(S), D).bytes;
 }
 
 // Shared checks and launch of the forward forms; `a` carries the
@@ -172,12 +173,22 @@ bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          uint16_t* out, void* workspace, size_t workspace_bytes,
                          bsattn_stream_t stream) {
   if (!q || !k || !v || !block_mask || !out) return BSATTN_ERR_NULL;
-  if (B > 0 && H > 0 && S > 0 && head_dim_ok(D)) {
-    const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
-  }
   PrefillArgs a = fwd_args(q, k, v, out, kSrcMask);
   a.mask = block_mask;
+  if (B > 0 && H > 0 && S > 0 && head_dim_ok(D)) {
+    const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
+    if (need > 0 && is_causal) {
+      if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0)
+        return BSATTN_ERR_WORKSPACE;
+      const SplitLayout L = split_layout(B, H, nblocks(S), D);
+      unsigned char* ws = (unsigned char*)workspace;
+      a.split_min = kSplitMinBlocks;
+      a.split_row0 = kSplitMinBlocks;   // causal row i holds at most i + 1 blocks
+      a.part_o = (float*)(ws + L.o_off);
+      a.part_ml = (float2*)(ws + L.ml_off);
+      a.part_flag = (int*)(ws + L.flag_off);
+    }
+  }
   return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 

@@ -39,8 +39,41 @@ struct PrefillArgs {
   int B, H, Sq, Sk, D, nbq, nbk;   // Sq <= Sk: the queries are the last Sq positions
   int causal;
   int ks;                // D = 64: key splits per work item, 1 or 2 (D = 128 always uses 2)
+  // Long causal rows split in two (kSrcMask, square only; split_min = 0: off).
+  // Query blocks i >= split_row0 can hold more than split_min key blocks; one
+  // extra work-group per such query block takes the second half of its list
+  // when it does, both halves leave fp32 partial rows in the workspace, and a
+  // merge launch writes those rows' output.  Slot s = bh * (nbq - split_row0)
+  // + (i - split_row0) of part_o [slots][2][64][D], part_ml [slots][2][64]
+  // (row max, row sum) and part_flag [slots] (1 when the row was split).
+  int split_min, split_row0;
+  float* part_o;
+  float2* part_ml;
+  int* part_flag;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Key blocks a causal row must exceed before bsattn_fwd splits it.
+constexpr int kSplitMinBlocks = 128;
+// Workspace of bsattn_fwd for the long-row split: zero when no causal row of
+// an nb-block square problem can exceed kSplitMinBlocks, or when the split
+// would need more than kSplitMaxBytes.
+constexpr size_t kSplitMaxBytes = size_t(2) << 30;
+struct SplitLayout {
+  int64_t slots;
+  size_t o_off, ml_off, flag_off, bytes;
+};
+inline SplitLayout split_layout(int B, int H, int nb, int D) {
+  SplitLayout L{};
+  if (nb <= kSplitMinBlocks) return L;
+  const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  L.slots = (int64_t)B * H * (nb - kSplitMinBlocks);
+  L.o_off = 0;
+  L.ml_off = up((size_t)L.slots * 2 * 64 * D * sizeof(float));
+  L.flag_off = L.ml_off + up((size_t)L.slots * 2 * 64 * sizeof(float2));
+  L.bytes = L.flag_off + up((size_t)L.slots * sizeof(int));
+  if (L.bytes > kSplitMaxBytes) L = SplitLayout{};
+  return L;
+}
 // LDS one forward work-group needs (K/V ring plus a block list of nbk entries).
 size_t prefill_lds_bytes(int D, int nbk);
 constexpr size_t kMaxLdsBytes = 160 * 1024;

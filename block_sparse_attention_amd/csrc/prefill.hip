@@ -171,7 +171,16 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   const int Sq = a.Sq, Sk = a.Sk;
   const int past = Sk - Sq;   // query row r sits at key position r + past
   int bh, i;
-  map_item(blockIdx.x, a.B * a.H, nbq, map_mode, group, bh, i);
+  // Work-groups below n_help take the second half of a long row's list (the
+  // query blocks i >= split_row0, heaviest first); the rest are the items.
+  const int n_help = a.split_min > 0 ? a.B * a.H * (nbq - a.split_row0) : 0;
+  const bool helper = (int)blockIdx.x < n_help;
+  if (helper) {
+    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, bh, i);
+    i += a.split_row0;
+  } else {
+    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, bh, i);
+  }
 
   const int64_t q_off = (int64_t)bh * Sq * D;
   const int64_t kv_off = (int64_t)bh * Sk * D;
@@ -208,13 +217,15 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   }
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds row qrow, dims 16s + 8h .. +8.
+  // (A helper loads it only once it knows its row is long.)
   u32x4 qf[C::kSteps];
-  {
+  auto load_q = [&]() {
     const int qr = min(qrow, Sq - 1);   // rows past the end are never stored
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
       qf[s] = *(const u32x4*)(Q + (int64_t)qr * D + 16 * s + 8 * h);
-  }
+  };
+  if (!helper) load_q();
 
   // ---- this query block's list of key blocks, ascending, into LDS ----
   // From a mask row, a given list, or (fused) a block-score row: the row is
@@ -298,7 +309,31 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     if (lane == 0) list[nbk] = (uint16_t)count;   // the slot after the list holds its length
   }
   __syncthreads();
-  const int nblk = __builtin_amdgcn_readfirstlane((int)list[nbk]);
+  int nblk = __builtin_amdgcn_readfirstlane((int)list[nbk]);
+  // A long row: the item takes the first half of the list, its helper the
+  // second; a helper whose row is not long has nothing to do.
+  int part = -1;   // -1: the whole row, written to out
+  int64_t slot = 0;
+  if constexpr (SRC == kSrcMask) {
+    if (a.split_min > 0 && i >= a.split_row0) {
+      slot = (int64_t)bh * (nbq - a.split_row0) + (i - a.split_row0);
+      const bool split = nblk > a.split_min;
+      if (!helper && tid == 0) a.part_flag[slot] = split ? 1 : 0;
+      if (!split && helper) return;
+      if (split) {
+        const int first = nblk >> 1;
+        if (helper) {
+          load_q();
+          part = 1;
+          list += first;
+          nblk -= first;
+        } else {
+          part = 0;
+          nblk = first;
+        }
+      }
+    }
+  }
 
   // ---- per-lane DMA source byte offsets for this wave's share of a tile ----
   // Instruction kk covers tile rows kk*kRowsPerInstr .. +kRowsPerInstr-1; lane l
@@ -638,7 +673,20 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     // one wave holds the whole row: normalise and store
     const float lt = sum_with_half_swap(l);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (qrow < Sq) {
+    if (qrow < Sq && part >= 0) {
+      // half of a long row: its normalised fp32 output and (row max, row sum)
+      const int64_t pr = (slot * 2 + part) * 64 + 32 * rg + n;
+      float* __restrict__ P = a.part_o + pr * D;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * t + 8 * g4 + 4 * h;
+          *(float4*)(P + d) = float4{o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv,
+                                     o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv};
+        }
+      if (h == 0) a.part_ml[pr] = float2{m, lt};
+    } else if (qrow < Sq) {
       uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t)
@@ -677,6 +725,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   const float lt = l_a * al_a + l_b * al_b;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   const float fa = al_a * inv, fb = al_b * inv;
+  // half of a long row: its normalised fp32 output and (row max, row sum)
+  const int64_t pr = (slot * 2 + (part < 0 ? 0 : part)) * 64 + 32 * rg + n;
   auto finish = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
     uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
@@ -692,10 +742,14 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
           r4[e] = o[kBase + t][ii] * fa + xin[(t * 16 + ii) * kWave + lane] * fb;
         }
         const int d = 32 * (kBase + t) + 8 * g4 + 4 * h;
-        *(u32x2*)(O + d) = u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
+        if (part >= 0)
+          *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+        else
+          *(u32x2*)(O + d) = u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
       }
     }
   };
+  if (part >= 0 && qrow < Sq && kh == 0 && h == 0) a.part_ml[pr] = float2{M, lt};
   if (qrow < Sq) {
     if (kh == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
@@ -711,6 +765,39 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         if (j < nbk) mo[j] = (uint8_t)((selbits[u] >> lane) & 1ull);
       }
     }
+  }
+}
+
+// Output rows of the long rows split in two: each half left its normalised
+// fp32 rows and (row max m, row sum l); the row is their weighted mean with
+// weights l * 2^((m - max m) * c), the same log-sum-exp combination the
+// split-KV decode's merge uses.  One work-group per slot; a slot whose row
+// was not split (flag 0) was written by its item.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_split_merge_kernel(PrefillArgs a, float c) {
+  const int64_t slot = blockIdx.x;
+  if (a.part_flag[slot] == 0) return;
+  const int per_bh = a.nbq - a.split_row0;
+  const int bh = (int)(slot / per_bh);
+  const int i = a.split_row0 + (int)(slot - (int64_t)bh * per_bh);
+  constexpr int kVec = D / 4;
+  for (int e = threadIdx.x; e < 64 * kVec; e += 256) {
+    const int r = e / kVec, d = 4 * (e - r * kVec);
+    const int qrow = 64 * i + r;
+    if (qrow >= a.Sq) break;   // rows ascend with e
+    const int64_t p0 = (slot * 2) * 64 + r, p1 = p0 + 64;
+    const float2 s0 = a.part_ml[p0], s1 = a.part_ml[p1];
+    const float mx = fmaxf(s0.x, s1.x);
+    const float w0 = s0.y * fast_exp2((s0.x - mx) * c);
+    const float w1 = s1.y * fast_exp2((s1.x - mx) * c);
+    const float tot = w0 + w1;
+    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+    const float f0 = w0 * inv, f1 = w1 * inv;
+    const float4 x0 = *(const float4*)(a.part_o + p0 * D + d);
+    const float4 x1 = *(const float4*)(a.part_o + p1 * D + d);
+    uint16_t* O = a.out + ((int64_t)bh * a.Sq + qrow) * D + d;
+    *(u32x2*)O = u32x2{pack_bf16x2(x0.x * f0 + x1.x * f1, x0.y * f0 + x1.y * f1),
+                       pack_bf16x2(x0.z * f0 + x1.z * f1, x0.w * f0 + x1.w * f1)};
   }
 }
 
@@ -744,9 +831,17 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int64_t items = (int64_t)BH * a.nbq;
+  const int64_t slots = a.split_min > 0 ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
+  const int64_t items = (int64_t)BH * a.nbq + slots;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
                      group);
+  if (slots > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float c = (float)(1.4426950408889634 / std::sqrt((double)D));
+    hipLaunchKernelGGL(prefill_split_merge_kernel<D>, dim3((unsigned)slots), dim3(256), 0, stream,
+                       a, c);
+  }
   return hipGetLastError();
 }
 

@@ -109,10 +109,24 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
  * before the P.V product, output rounded to nearest even).  A row that sees
  * no key is written as zeros.  Each query block's mask row is compacted on
  * the device into its ascending active-block list before the block loop.
- * workspace may be NULL when bsattn_fwd_workspace_bytes returns 0.
+ * With is_causal, a query block whose list holds more than 128 key blocks
+ * is split in two: a second work-group takes the second half of its list,
+ * both halves leave fp32 rows and their (row max, row sum) in the workspace,
+ * and a merge launch writes the row as the log-sum-exp weighted mean of the
+ * halves (the combination of the split-KV decode, same guide, §6.2), so no
+ * row runs far longer than the rest.  The result differs from the unsplit
+ * pass only by fp32 rounding.
+ * workspace: device memory of bsattn_fwd_workspace_bytes bytes, 16-byte
+ * aligned, used by causal calls only (may be NULL when that size is 0);
+ * calls that overlap in time need workspaces of their own.
  * Errors: NULL pointers; B, H, S <= 0 (SHAPE); D not 64 or 128 (UNSUPPORTED);
- * workspace_bytes below bsattn_fwd_workspace_bytes (WORKSPACE).
+ * workspace NULL, misaligned or below bsattn_fwd_workspace_bytes (WORKSPACE).
  */
+/* Workspace of bsattn_fwd: nonzero when S spans more than 128 key blocks
+ * (B * H * (nb - 128) query blocks can split, each needing two fp32
+ * [64, D] halves, 2 x 64 (row max, row sum) pairs and a flag, every part
+ * 256-byte aligned); 0 when no row can split, when the split would need more
+ * than 2 GiB (such calls then run unsplit), or for arguments out of range. */
 size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D);
 
 bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -139,7 +153,10 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
  * last two rows; tril; forced diagonal), writes that row to mask_out when
  * mask_out is not NULL (uint8 0/1 [B, H, nb, nb], byte-identical to the
  * builders' output), compacts it, and runs the forward pass of bsattn_fwd on
- * it.  q/k/v/out and is_causal as bsattn_fwd.
+ * it, every row whole in one work-group (no long-row split, so the output is
+ * bit-identical to bsattn_fwd_chunk with Sq = Sk on that mask, and to
+ * bsattn_fwd wherever bsattn_fwd does not split).  q/k/v/out and is_causal as
+ * bsattn_fwd.
  * Errors: as bsattn_fwd and the builders (topk < 0 or topk > nb: SHAPE);
  * nb > 256 (S > 16384: the row's keys are held in registers) is UNSUPPORTED,
  * where the two-launch path (builder, then bsattn_fwd) applies.

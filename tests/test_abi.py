@@ -66,6 +66,27 @@ def test_fwd_validates_on_host():
     assert lib.bsattn_fwd_workspace_bytes(2, 16, 4096, 64) == 0
 
 
+def test_fwd_long_row_workspace_on_host():
+    """Causal rows past 128 key blocks split in two through the workspace."""
+    lib = _lib()
+    F = FAKE
+    S = 8320                       # 130 key blocks: query blocks 128 and 129 can split
+    need = lib.bsattn_fwd_workspace_bytes(1, 8, S, 128)
+    slots = 8 * 2
+    assert need >= slots * (2 * 64 * 128 * 4 + 2 * 64 * 8 + 4) and need % 256 == 0
+    assert lib.bsattn_fwd_workspace_bytes(1, 8, S, 64) < need      # halves of D = 64 rows
+    assert lib.bsattn_fwd(F, F, F, F, 1, 8, S, 128, 1, F, None, 0, None) == 4
+    assert lib.bsattn_fwd(F, F, F, F, 1, 8, S, 128, 1, F, F, need - 1, None) == 4
+    misaligned = ctypes.c_void_p(0x1008)
+    assert lib.bsattn_fwd(F, F, F, F, 1, 8, S, 128, 1, F, misaligned, need, None) == 4
+    assert lib.bsattn_fwd_workspace_bytes(1, 8, 8192, 128) == 0    # 128 blocks: no row can exceed 128
+    assert lib.bsattn_fwd_workspace_bytes(1, 8, 8193, 128) > 0
+    assert lib.bsattn_fwd_workspace_bytes(0, 8, S, 128) == 0
+    assert lib.bsattn_fwd_workspace_bytes(1, 8, S, 96) == 0
+    # beyond 2 GiB the long rows run unsplit and no workspace is asked for
+    assert lib.bsattn_fwd_workspace_bytes(64, 64, 65536, 128) == 0
+
+
 def test_decode_validates_on_host():
     lib = _lib()
     F = FAKE

@@ -215,3 +215,41 @@ def test_rising_scores_take_the_rescale_path(B, H, D, dense):
         fused = bsa.bsattn_fwd_topk(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
                                     to_gpu(np.zeros((B, H, nb, nb), np.float32)), nb)
         check_close(gpu_bf16_to_f64(fused), want, f"rising scores fused B{B} H{H} D{D}")
+
+
+def _long_row_mask(H, nb, seed, heavy=True):
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((1, H, nb, nb)) < 0.05).astype(np.uint8)
+    mask[..., np.arange(nb), np.arange(nb)] = 1
+    if heavy:
+        for h in range(H - 1):          # the last head keeps light rows: its helpers have nothing to do
+            mask[0, h, 128, :129] = 1   # 129 blocks: split 64 / 65
+            mask[0, h, 129, :130] = 1   # 130 blocks: split 65 / 65
+            if h % 2:
+                mask[0, h, 129, [3, 77]] = 0   # exactly 128 blocks: not split
+    return mask
+
+
+@pytest.mark.parametrize("S", [8320, 8300])
+@pytest.mark.parametrize("H,D", [(8, 64), (4, 64), (8, 128)])
+def test_long_rows_split_in_two(S, H, D):
+    """Causal query blocks with more than 128 key blocks run as two halves and a
+    merge; one workspace serves a call with long rows, then one without (the
+    split flags of the first must not leak into the second)."""
+    import torch
+    nb = -(-S // 64)
+    need = bsa.bsattn_fwd_workspace_bytes(1, H, S, D)
+    assert need > 0
+    rng = np.random.default_rng(S + H + D)
+    qkv = {n: gen.f32_to_bf16_bits(rng.standard_normal((1, H, S, D), dtype=np.float32)) for n in ("q", "k", "v")}
+    q, k, v = (to_gpu_bf16(qkv[n]) for n in ("q", "k", "v"))
+    x = _f64(qkv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    rows = sorted(set(range(128 * 64, S)) | {0, 64 * 127, 64 * 127 + 63, S // 2})
+    for heavy in (True, False):
+        mask = _long_row_mask(H, nb, seed=S * 7 + D, heavy=heavy)
+        say(f"[prefill] long rows S={S} H={H} D={D} heavy={heavy} blocks={int(mask.sum())}")
+        got = gpu_bf16_to_f64(bsa.bsattn_fwd(q, k, v, to_gpu(mask), True, workspace=ws))
+        want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], mask[0, h], True, rows)
+                         for h in range(H)])
+        check_close(got[0][:, rows], want, f"S{S} H{H} D{D} heavy={heavy}")

@@ -2,7 +2,10 @@
 
 bsattn_fwd_topk / bsattn_fwd_threshold must write the same mask bytes as the
 stand-alone builders (and as the oracle), and produce outputs bit-identical
-to bsattn_fwd on that mask (the same block lists in the same order)."""
+to the mask-driven forward pass on that mask when it runs every row whole
+(the chunk entry with Sq = Sk: the same block lists in the same order).
+bsattn_fwd, which splits causal rows of more than 128 key blocks in two,
+agrees with them within the output tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +13,7 @@ import torch
 import block_sparse_attention_amd as bsa
 from block_sparse_attention_amd import inputs as gen
 from oracle import mask as om
-from tests.gpu_util import say, to_gpu, to_gpu_bf16
+from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +26,9 @@ def _both(q, k, v, scores, cfg_kind, param, dense2, diag, causal):
     else:
         m = bsa.bsattn_build_mask_threshold(s, param, dense2, diag)
         fused, fm = bsa.bsattn_fwd_threshold(q, k, v, s, param, dense2, diag, causal, write_mask=True)
-    ref = bsa.bsattn_fwd(q, k, v, m, causal)
+    ref = bsa.bsattn_fwd_chunk(q, k, v, m, causal)
+    split = bsa.bsattn_fwd(q, k, v, m, causal)
+    check_close(gpu_bf16_to_f64(split), gpu_bf16_to_f64(ref), "bsattn_fwd against whole rows")
     return m, ref, fm, fused
 
 
