@@ -771,33 +771,57 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 // Output rows of the long rows split in two: each half left its normalised
 // fp32 rows and (row max m, row sum l); the row is their weighted mean with
 // weights l * 2^((m - max m) * c), the same log-sum-exp combination the
-// split-KV decode's merge uses.  One work-group per slot; a slot whose row
-// was not split (flag 0) was written by its item.
+// split-KV decode's merge uses.  One work-group per 64 slots: every wave reads
+// the 64 flags (a slot whose row was not split, flag 0, was written by its
+// item), then the work-group merges the flagged slots one after another.
+constexpr int kMergeSlots = 64;
 template <int D>
 __global__ __launch_bounds__(256) void prefill_split_merge_kernel(PrefillArgs a, float c) {
-  const int64_t slot = blockIdx.x;
-  if (a.part_flag[slot] == 0) return;
   const int per_bh = a.nbq - a.split_row0;
-  const int bh = (int)(slot / per_bh);
-  const int i = a.split_row0 + (int)(slot - (int64_t)bh * per_bh);
-  constexpr int kVec = D / 4;
-  for (int e = threadIdx.x; e < 64 * kVec; e += 256) {
-    const int r = e / kVec, d = 4 * (e - r * kVec);
-    const int qrow = 64 * i + r;
-    if (qrow >= a.Sq) break;   // rows ascend with e
-    const int64_t p0 = (slot * 2) * 64 + r, p1 = p0 + 64;
-    const float2 s0 = a.part_ml[p0], s1 = a.part_ml[p1];
-    const float mx = fmaxf(s0.x, s1.x);
-    const float w0 = s0.y * fast_exp2((s0.x - mx) * c);
-    const float w1 = s1.y * fast_exp2((s1.x - mx) * c);
-    const float tot = w0 + w1;
-    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    const float f0 = w0 * inv, f1 = w1 * inv;
-    const float4 x0 = *(const float4*)(a.part_o + p0 * D + d);
-    const float4 x1 = *(const float4*)(a.part_o + p1 * D + d);
-    uint16_t* O = a.out + ((int64_t)bh * a.Sq + qrow) * D + d;
-    *(u32x2*)O = u32x2{pack_bf16x2(x0.x * f0 + x1.x * f1, x0.y * f0 + x1.y * f1),
-                       pack_bf16x2(x0.z * f0 + x1.z * f1, x0.w * f0 + x1.w * f1)};
+  const int64_t slots = (int64_t)a.B * a.H * per_bh;
+  const int64_t s0 = (int64_t)blockIdx.x * kMergeSlots;
+  const int lane = threadIdx.x & 63;
+  const bool in = s0 + lane < slots;
+  uint64_t todo = wave_ballot(in && a.part_flag[in ? s0 + lane : 0] != 0);
+  constexpr int kVec = D / 4;               // float4 per row
+  constexpr int kIt = 64 * kVec / 256;      // float4 per thread and half
+  while (todo) {
+    const int64_t slot = s0 + __ffsll((unsigned long long)todo) - 1;
+    todo &= todo - 1;
+    const int bh = (int)(slot / per_bh);
+    const int i = a.split_row0 + (int)(slot - (int64_t)bh * per_bh);
+    // Every load first (rows past Sq read workspace the halves left
+    // unwritten, inside the allocation; their results are not stored).
+    float4 x0[kIt], x1[kIt];
+    float2 m0[kIt], m1[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = threadIdx.x + 256 * it;
+      const int r = e / kVec, d = 4 * (e % kVec);
+      const int64_t p0 = slot * 128 + r, p1 = p0 + 64;
+      x0[it] = *(const float4*)(a.part_o + p0 * D + d);
+      x1[it] = *(const float4*)(a.part_o + p1 * D + d);
+      m0[it] = a.part_ml[p0];
+      m1[it] = a.part_ml[p1];
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = threadIdx.x + 256 * it;
+      const int r = e / kVec, d = 4 * (e % kVec);
+      const int qrow = 64 * i + r;
+      if (qrow < a.Sq) {
+        const float mx = fmaxf(m0[it].x, m1[it].x);
+        const float w0 = m0[it].y * fast_exp2((m0[it].x - mx) * c);
+        const float w1 = m1[it].y * fast_exp2((m1[it].x - mx) * c);
+        const float tot = w0 + w1;
+        const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+        const float f0 = w0 * inv, f1 = w1 * inv;
+        const float4 u = x0[it], v = x1[it];
+        uint16_t* O = a.out + ((int64_t)bh * a.Sq + qrow) * D + d;
+        *(u32x2*)O = u32x2{pack_bf16x2(u.x * f0 + v.x * f1, u.y * f0 + v.y * f1),
+                           pack_bf16x2(u.z * f0 + v.z * f1, u.w * f0 + v.w * f1)};
+      }
+    }
   }
 }
 
@@ -839,8 +863,9 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float c = (float)(1.4426950408889634 / std::sqrt((double)D));
-    hipLaunchKernelGGL(prefill_split_merge_kernel<D>, dim3((unsigned)slots), dim3(256), 0, stream,
-                       a, c);
+    hipLaunchKernelGGL(prefill_split_merge_kernel<D>,
+                       dim3((unsigned)((slots + kMergeSlots - 1) / kMergeSlots)), dim3(256), 0,
+                       stream, a, c);
   }
   return hipGetLastError();
 }
