@@ -202,7 +202,11 @@ def _qkv(q, k, v):
 
 
 def bsattn_fwd(q, k, v, block_mask, is_causal: bool = True, out=None, workspace=None, stream=None):
-    """Block-sparse attention forward (guide §4).  q,k,v bf16 [B,H,S,D]; mask uint8 [B,H,nb,nb]."""
+    """Block-sparse attention forward (guide §4).  q,k,v bf16 [B,H,S,D]; mask uint8 [B,H,nb,nb].
+
+    Causal calls with more than 128 key blocks split long rows in two and need
+    a device workspace of bsattn_fwd_workspace_bytes(B, H, S, D) bytes; when
+    `workspace` is None one is allocated for the call."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     _dev(block_mask, "block_mask", torch.uint8, 4)
