@@ -253,3 +253,22 @@ def test_long_rows_split_in_two(S, H, D):
         want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], mask[0, h], True, rows)
                          for h in range(H)])
         check_close(got[0][:, rows], want, f"S{S} H{H} D{D} heavy={heavy}")
+
+
+def test_long_rows_noncausal_run_whole():
+    """Non-causal calls never split (every row may see every block): no
+    workspace is passed, and rows of 130 blocks run whole."""
+    S, H, D = 8300, 4, 64
+    nb = -(-S // 64)
+    assert bsa.bsattn_fwd_workspace_bytes(1, H, S, D) > 0
+    rng = np.random.default_rng(77)
+    qkv = {n: gen.f32_to_bf16_bits(rng.standard_normal((1, H, S, D), dtype=np.float32)) for n in ("q", "k", "v")}
+    mask = (rng.random((1, H, nb, nb)) < 0.05).astype(np.uint8)
+    mask[0, :, 127:] = 1                # dense rows, past the diagonal too
+    say(f"[prefill] long rows non-causal S={S} H={H} D={D} blocks={int(mask.sum())}")
+    got = _run_gpu(qkv, mask, False)
+    x = _f64(qkv)
+    rows = sorted(set(range(127 * 64, S)) | {0, 1, S // 2})
+    want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], mask[0, h], False, rows)
+                     for h in range(H)])
+    check_close(got[0][:, rows], want, "long rows non-causal")
