@@ -43,6 +43,11 @@
 // * Work items are issued heaviest-first (last query block first), and when
 //   batch*heads is a multiple of 8 each head's items stay on one XCD so its
 //   K/V stay in that XCD's L2.
+// * Long causal rows (more than split_min key blocks, when the caller gives a
+//   workspace) run as two halves in two work-groups; each leaves fp32 rows
+//   plus (row max, row sum), and a small merge launch combines them by the
+//   log-sum-exp rule of the split-KV decode (TileLang block-sparse guide,
+//   §6.2), so a few dense rows do not hold up the whole launch.
 #include <math.h>
 
 #include <algorithm>
