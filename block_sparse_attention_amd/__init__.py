@@ -138,6 +138,18 @@ def _stream(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A new device tensor owned by the stream the call runs on.  The caching
+    allocator then hands its memory to another stream only after the work
+    queued on `stream` is done with it, so temporaries (workspaces) dropped
+    on return stay intact while the kernels still read or write them."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _ptr(t) -> int:
     return int(t.data_ptr())
 
@@ -151,7 +163,7 @@ def bsattn_build_mask_topk(scores, topk: int, dense_last_two_rows: bool = False,
     if nb != nb2:
         raise ValueError("scores must be [B, H, nb, nb]")
     if out is None:
-        out = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=scores.device)
+        out = _empty((B, H, nb, nb), torch.uint8, scores.device, stream)
     _dev(out, "out", torch.uint8, 4)
     _check("bsattn_build_mask_topk", load_library().bsattn_build_mask_topk(
         _ptr(scores), B, H, nb, int(topk), int(bool(dense_last_two_rows)),
@@ -168,7 +180,7 @@ def bsattn_build_mask_threshold(scores, threshold: float, dense_last_two_rows: b
     if nb != nb2:
         raise ValueError("scores must be [B, H, nb, nb]")
     if out is None:
-        out = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=scores.device)
+        out = _empty((B, H, nb, nb), torch.uint8, scores.device, stream)
     _dev(out, "out", torch.uint8, 4)
     _check("bsattn_build_mask_threshold", load_library().bsattn_build_mask_threshold(
         _ptr(scores), B, H, nb, float(threshold), int(bool(dense_last_two_rows)),
@@ -176,13 +188,21 @@ def bsattn_build_mask_threshold(scores, threshold: float, dense_last_two_rows: b
     return out
 
 
-def bsattn_mask_to_indices(mask, is_causal: bool = True, stream=None) -> Tuple[object, object]:
-    """uint8 mask [B,H,nb,nb] -> (idx int32 [B,H,nb,nb] ascending, -1 padded; cnt int32 [B,H,nb])."""
+def bsattn_mask_to_indices(mask, is_causal: bool = True, idx=None, cnt=None,
+                           stream=None) -> Tuple[object, object]:
+    """uint8 mask [B,H,nb,nb] -> (idx int32 [B,H,nb,nb] ascending, -1 padded; cnt int32 [B,H,nb]).
+    idx / cnt may be given (written in place)."""
     torch = _torch()
     _dev(mask, "mask", torch.uint8, 4)
     B, H, nb, _ = mask.shape
-    idx = torch.empty((B, H, nb, nb), dtype=torch.int32, device=mask.device)
-    cnt = torch.empty((B, H, nb), dtype=torch.int32, device=mask.device)
+    if idx is None:
+        idx = _empty((B, H, nb, nb), torch.int32, mask.device, stream)
+    if cnt is None:
+        cnt = _empty((B, H, nb), torch.int32, mask.device, stream)
+    _dev(idx, "idx", torch.int32, 4)
+    _dev(cnt, "cnt", torch.int32, 3)
+    if tuple(idx.shape) != (B, H, nb, nb) or tuple(cnt.shape) != (B, H, nb):
+        raise ValueError("idx must be [B,H,nb,nb] and cnt [B,H,nb]")
     _check("bsattn_mask_to_indices", load_library().bsattn_mask_to_indices(
         _ptr(mask), B, H, nb, int(bool(is_causal)), _ptr(idx), _ptr(cnt), _stream(stream)))
     return idx, cnt
@@ -214,13 +234,13 @@ def bsattn_fwd(q, k, v, block_mask, is_causal: bool = True, out=None, workspace=
     if tuple(block_mask.shape) != (B, H, nb, nb):
         raise ValueError(f"block_mask must be [{B}, {H}, {nb}, {nb}]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
     need = bsattn_fwd_workspace_bytes(B, H, S, D)
     ws_ptr, ws_bytes = 0, 0
     if need and (is_causal or workspace is not None):
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _empty(need, torch.uint8, q.device, stream)
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check("bsattn_fwd", load_library().bsattn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), B, H, S, D, int(bool(is_causal)),
@@ -238,7 +258,7 @@ def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stre
     if tuple(idx.shape) != (B, H, nb, nb) or tuple(cnt.shape) != (B, H, nb):
         raise ValueError("idx must be [B,H,nb,nb] and cnt [B,H,nb]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
     _check("bsattn_fwd_indices", load_library().bsattn_fwd_indices(
         _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), B, H, S, D, int(bool(is_causal)),
@@ -246,7 +266,7 @@ def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stre
     return out
 
 
-def _fused_setup(q, k, v, scores, out, mask_out, write_mask):
+def _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream):
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     nb = -(-S // BLOCK)
@@ -254,11 +274,11 @@ def _fused_setup(q, k, v, scores, out, mask_out, write_mask):
     if tuple(scores.shape) != (B, H, nb, nb):
         raise ValueError("block scores must be [B, H, nb, nb]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
     mask = mask_out
     if mask is None and write_mask:
-        mask = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=q.device)
+        mask = _empty((B, H, nb, nb), torch.uint8, q.device, stream)
     if mask is not None:
         _dev(mask, "mask_out", torch.uint8, 4)
         if tuple(mask.shape) != (B, H, nb, nb):
@@ -272,7 +292,7 @@ def bsattn_fwd_topk(q, k, v, scores, topk: int, dense_last_two_rows: bool = Fals
     """Top-k mask build + compaction + forward in one launch (guide §3.1, §4).
     The mask goes to mask_out when given (or to a new tensor with write_mask).
     Returns out, or (out, mask) with write_mask."""
-    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask)
+    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream)
     _check("bsattn_fwd_topk", load_library().bsattn_fwd_topk(
         _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, int(topk),
         int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
@@ -284,7 +304,7 @@ def bsattn_fwd_threshold(q, k, v, scores, threshold: float, dense_last_two_rows:
                          force_diagonal: bool = True, is_causal: bool = True, out=None,
                          mask_out=None, write_mask: bool = False, stream=None):
     """Threshold mask build + compaction + forward in one launch (guide §3.2, §4)."""
-    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask)
+    B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream)
     _check("bsattn_fwd_threshold", load_library().bsattn_fwd_threshold(
         _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, float(threshold),
         int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
@@ -310,7 +330,7 @@ def bsattn_fwd_chunk(q, k, v, block_mask, is_causal: bool = True, out=None, stre
     if tuple(block_mask.shape) != (B, H, -(-Sq // BLOCK), -(-Sk // BLOCK)):
         raise ValueError("block_mask must be [B, H, ceil(Sq/64), ceil(Sk/64)]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
     _check("bsattn_fwd_chunk", load_library().bsattn_fwd_chunk(
         _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), B, H, Sq, Sk, D, int(bool(is_causal)),
@@ -331,7 +351,7 @@ def bsattn_decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> i
     return int(load_library().bsattn_decode_workspace_bytes(B, Hq, D, num_splits))
 
 
-def _decode_common(q, Hkv, slots, num_splits, out, workspace):
+def _decode_common(q, Hkv, slots, num_splits, out, workspace, stream):
     torch = _torch()
     B, Hq, D = q.shape
     ns = int(num_splits)
@@ -340,13 +360,13 @@ def _decode_common(q, Hkv, slots, num_splits, out, workspace):
         if ns <= 0:
             raise BsattnError("bsattn_decode_default_splits", 5, "could not query the device")
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = _empty((B, Hq, D), torch.bfloat16, q.device, stream)
     _dev(out, "out", torch.bfloat16, 3)
     need = bsattn_decode_workspace_bytes(B, Hq, D, ns)
     ws_ptr, ws_bytes = 0, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _empty(need, torch.uint8, q.device, stream)
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     return ns, out, ws_ptr, ws_bytes
 
@@ -376,7 +396,7 @@ def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0,
     if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
         raise ValueError("block_indices must be [B, Hkv, max_sel]")
     max_sel = block_indices.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa", load_library().bsattn_decode_gqa(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
         max_sel, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
@@ -395,7 +415,7 @@ def bsattn_decode_gqa_mask(q, k, v, cu_seqlens_k, block_mask, num_splits: int = 
     if block_mask.shape[0] != B or block_mask.shape[1] != Hkv:
         raise ValueError("block_mask must be [B, Hkv, num_blocks]")
     nblocks = block_mask.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, nblocks, num_splits, out, workspace)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, nblocks, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa_mask", load_library().bsattn_decode_gqa_mask(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_mask), B, Hq, Hkv, D,
         nblocks, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
@@ -423,7 +443,7 @@ def bsattn_decode_gqa_paged(q, k_cache, v_cache, cache_seqlens, block_table, blo
     if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
         raise ValueError("block_indices must be [B, Hkv, max_sel]")
     max_sel = block_indices.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa_paged", load_library().bsattn_decode_gqa_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
         _ptr(block_indices), B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1], max_sel,
@@ -447,11 +467,11 @@ def _xattn_qk(q, k):
     return B, H, Sq, k.shape[2], D
 
 
-def _xattn_ws(B, H, Sq, Sk, stride, workspace, device):
+def _xattn_ws(B, H, Sq, Sk, stride, workspace, device, stream):
     torch = _torch()
     need = bsattn_xattn_workspace_bytes(B, H, Sq, Sk, stride)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        workspace = _empty(max(need, 1), torch.uint8, device, stream)
     return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
@@ -463,9 +483,9 @@ def bsattn_xattn_block_sums(q, k, stride: int = 8, norm: float = 1.0, is_causal:
     B, H, Sq, Sk, D = _xattn_qk(q, k)
     nbq, nbk = -(-Sq // BLOCK), -(-Sk // BLOCK)
     if out is None:
-        out = torch.empty((B, H, nbq, nbk), dtype=torch.float32, device=q.device)
+        out = _empty((B, H, nbq, nbk), torch.float32, q.device, stream)
     _dev(out, "out", torch.float32, 4)
-    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device)
+    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device, stream)
     _check("bsattn_xattn_block_sums", load_library().bsattn_xattn_block_sums(
         _ptr(q), _ptr(k), B, H, Sq, Sk, D, int(stride), float(norm), int(bool(is_causal)),
         _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
@@ -481,7 +501,7 @@ def bsattn_build_mask_cumulative(block_sums, threshold: float = 0.9, keep_sink: 
     _dev(block_sums, "block_sums", torch.float32, 4)
     B, H, nbq, nbk = block_sums.shape
     if out is None:
-        out = torch.empty((B, H, nbq, nbk), dtype=torch.uint8, device=block_sums.device)
+        out = _empty((B, H, nbq, nbk), torch.uint8, block_sums.device, stream)
     _dev(out, "out", torch.uint8, 4)
     _check("bsattn_build_mask_cumulative", load_library().bsattn_build_mask_cumulative(
         _ptr(block_sums), B, H, nbq, nbk, float(threshold), int(bool(keep_sink)),
@@ -499,13 +519,13 @@ def bsattn_xattn_estimate(q, k, stride: int = 8, norm: float = 1.0, threshold: f
     B, H, Sq, Sk, D = _xattn_qk(q, k)
     nbq, nbk = -(-Sq // BLOCK), -(-Sk // BLOCK)
     if out is None:
-        out = torch.empty((B, H, nbq, nbk), dtype=torch.uint8, device=q.device)
+        out = _empty((B, H, nbq, nbk), torch.uint8, q.device, stream)
     _dev(out, "out", torch.uint8, 4)
     if block_sums is None and write_sums:
-        block_sums = torch.empty((B, H, nbq, nbk), dtype=torch.float32, device=q.device)
+        block_sums = _empty((B, H, nbq, nbk), torch.float32, q.device, stream)
     if block_sums is not None:
         _dev(block_sums, "block_sums", torch.float32, 4)
-    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device)
+    ws_ptr, ws_bytes = _xattn_ws(B, H, Sq, Sk, stride, workspace, q.device, stream)
     _check("bsattn_xattn_estimate", load_library().bsattn_xattn_estimate(
         _ptr(q), _ptr(k), B, H, Sq, Sk, D, int(stride), float(norm), float(threshold),
         int(bool(keep_sink)), int(bool(keep_diagonal)), int(bool(is_causal)),

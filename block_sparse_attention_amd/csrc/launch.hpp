@@ -5,7 +5,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bsattn {
+
+// Host side: the largest value a kernel attribute has been raised to on each
+// device, so a launcher sets it only when a call needs more than any earlier
+// call did (devices 0..63; on others it is set on every call).  Instances
+// must have static storage duration (zero-initialised).  Concurrent first
+// calls may both set the attribute, which is harmless.
+struct DeviceHighWater {
+  std::atomic<int> level[64];
+  template <class F>
+  hipError_t raise_to(int v, F&& set) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < 64;
+    if (cached && level[dev].load(std::memory_order_acquire) >= v) return hipSuccess;
+    e = set(v);
+    if (e == hipSuccess && cached) {
+      int cur = level[dev].load(std::memory_order_relaxed);
+      while (cur < v && !level[dev].compare_exchange_weak(cur, v, std::memory_order_acq_rel)) {
+      }
+    }
+    return e;
+  }
+};
 
 hipError_t launch_mask_topk(const float* scores, int B, int H, int nb, int topk, int dense2,
                             int diag, uint8_t* mask, hipStream_t stream);

@@ -178,7 +178,10 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   int bh, i;
   // Work-groups below n_help take the second half of a long row's list (the
   // query blocks i >= split_row0, heaviest first); the rest are the items.
-  const int n_help = a.split_min > 0 ? a.B * a.H * (nbq - a.split_row0) : 0;
+  // Only a mask-row source splits (the split logic below is compiled for it
+  // alone), so any other source has no helpers whatever split_min says.
+  const int n_help =
+      (SRC == kSrcMask && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
   const bool helper = (int)blockIdx.x < n_help;
   if (helper) {
     map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, bh, i);
@@ -856,11 +859,15 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const size_t lds = lds_bytes<D, KS>(a.nbk);
   auto kern = prefill_kernel<D, KS, CAUSAL, SRC>;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static DeviceHighWater lds_set;   // per instantiation and device
+    hipError_t e = lds_set.raise_to((int)lds, [&](int v) {
+      return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+    });
     if (e != hipSuccess) return e;
   }
-  const int64_t slots = a.split_min > 0 ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
+  // helpers and the merge exist only for the mask-row source
+  const int64_t slots =
+      (SRC == kSrcMask && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
   const int64_t items = (int64_t)BH * a.nbq + slots;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
                      group);

@@ -500,8 +500,10 @@ hipError_t launch_xattn_ds(const XattnArgs& a, hipStream_t stream) {
   using T = XTile<kXWT>;
   auto kern = xattn_lse_kernel<D, S, kXWT>;
   if (T::kLdsBytes > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+    static DeviceHighWater lds_set;   // per instantiation and device
+    hipError_t e = lds_set.raise_to((int)T::kLdsBytes, [&](int v) {
+      return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+    });
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(T::kThreads), T::kLdsBytes, stream, a);
@@ -548,8 +550,10 @@ hipError_t launch_cumulative_nu(const float* sums, int64_t rows, int nbq, int nb
   constexpr size_t lds = selection_lds_bytes<NU>();
   auto kern = mask_cumulative_kernel<NU>;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static DeviceHighWater lds_set;   // per instantiation and device
+    hipError_t e = lds_set.raise_to((int)lds, [&](int v) {
+      return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+    });
     if (e != hipSuccess) return e;
   }
   const int64_t groups = (rows + kSelRows - 1) / kSelRows;

@@ -3,11 +3,17 @@
  *
  * Plain C ABI.  Every tensor argument is a caller-owned, contiguous, row-major
  * DEVICE buffer; bfloat16 tensors are passed as their uint16 bit patterns.
- * The library never allocates device memory, keeps no mutable global state
- * and never synchronises the host: each call only enqueues kernels on
- * `stream` (a hipStream_t; NULL = the default stream).  Outputs are valid
- * once the stream reaches the end of the call.  Equal inputs give bitwise
- * equal outputs (no atomics on any value path).
+ * The library never allocates device memory and never synchronises the
+ * host: each call only enqueues kernels on `stream` (a hipStream_t; NULL =
+ * the default stream).  Outputs are valid once the stream reaches the end of
+ * the call.  Equal inputs give bitwise equal outputs (no atomics on any
+ * value path).
+ *
+ * Host state: the only state kept between calls is per device and
+ * write-once in effect — the device's compute-unit count (read on first use,
+ * for the default decode split count and the forward's launch shape) and
+ * the largest dynamic-LDS size each kernel has been granted.  Both are
+ * atomics, so the library is safe to call from several host threads.
  *
  * Errors: all argument checks run on the host BEFORE any launch.  On an
  * error nothing is enqueued and no output is touched.  A launch failure
@@ -114,8 +120,9 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
  * both halves leave fp32 rows and their (row max, row sum) in the workspace,
  * and a merge launch writes the row as the log-sum-exp weighted mean of the
  * halves (the combination of the split-KV decode, same guide, §6.2), so no
- * row runs far longer than the rest.  The result differs from the unsplit
- * pass only by fp32 rounding.
+ * row runs far longer than the rest.  A split row agrees with the unsplit
+ * pass within the output tolerance, not bit for bit: each half rounds its
+ * probabilities to bfloat16 against its own running exponent offset.
  * workspace: device memory of bsattn_fwd_workspace_bytes bytes, 16-byte
  * aligned, used by causal calls only (may be NULL when that size is 0);
  * calls that overlap in time need workspaces of their own.
@@ -160,6 +167,10 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
  * Errors: as bsattn_fwd and the builders (topk < 0 or topk > nb: SHAPE);
  * nb > 256 (S > 16384: the row's keys are held in registers) is UNSUPPORTED,
  * where the two-launch path (builder, then bsattn_fwd) applies.
+ * Speed: with more than 128 key blocks (S > 8192) and causal masks whose
+ * rows can hold more than 128 blocks, the two-launch path is the faster one,
+ * since only bsattn_fwd splits long rows; up to 128 blocks the two forms
+ * are within a few percent of each other.
  */
 bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* block_scores, int B, int H, int S, int D, int topk,
@@ -203,9 +214,12 @@ bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint1
 int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,
                              int num_cus);
 
-/* Workspace for bsattn_decode_gqa: fp32 partial outputs [B, Hq, splits, D]
- * and their base-2 log-sum-exp [B, Hq, splits], 256-byte aligned.  Returns 0
- * when an argument is out of range. */
+/* Workspace for bsattn_decode_gqa and its mask and paged forms: what the
+ * split stage hands the merge stage (same guide, §6.1: one partial output
+ * and one log-sum-exp per split) — fp32 partial outputs [B, Hq, splits, D]
+ * and their base-2 log-sum-exp [B, Hq, splits], each part 256-byte aligned.
+ * 0 when num_splits is 1 (the split kernel then writes out directly) or an
+ * argument is out of range. */
 size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
 /*

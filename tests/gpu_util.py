@@ -40,3 +40,20 @@ def check_close(got: np.ndarray, want: np.ndarray, what: str, max_abs=MAX_ABS, m
     assert mx <= max_abs, f"{what}: max abs err {mx} > {max_abs}"
     assert mn <= mean_abs, f"{what}: mean abs err {mn} > {mean_abs}"
     return mx, mn
+
+
+def parallel_map(fn, items, workers: int = 8):
+    """fn over items on a thread pool (numpy releases the GIL in its array
+    loops), BLAS single-threaded in each worker; results in item order."""
+    import concurrent.futures as cf
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except Exception:  # pragma: no cover
+        limit = None
+    try:
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, items))
+    finally:
+        if limit is not None and hasattr(limit, "restore_original_limits"):
+            limit.restore_original_limits()

@@ -7,7 +7,7 @@ import torch
 import block_sparse_attention_amd as bsa
 from block_sparse_attention_amd import inputs as gen
 from oracle import xattn as ox
-from tests.gpu_util import say, to_gpu, to_gpu_bf16
+from tests.gpu_util import parallel_map, say, to_gpu, to_gpu_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -160,9 +160,9 @@ def test_estimate_mask(B, H, Sq, Sk, D, stride, causal):
         np.testing.assert_array_equal(m2.cpu().numpy(), mask)
 
 
-def test_full_size_sampled_heads():
-    """The 16384-token, 32-head, D 128 prefill shape at stride 8: all heads on
-    the GPU, two heads against the oracle."""
+def test_full_size_every_head():
+    """The 16384-token, 32-head, D 128 prefill shape at stride 8: every head's
+    block sums against the oracle, and every head's selection valid for them."""
     cfg = gen.CONFIGS["C3"]
     qkv = gen.prefill_qkv(cfg, 0)
     q, k = to_gpu_bf16(qkv["q"]), to_gpu_bf16(qkv["k"])
@@ -171,10 +171,12 @@ def test_full_size_sampled_heads():
     sums = sums.cpu().numpy()
     mask = mask.cpu().numpy()
     f = gen.bf16_bits_to_f64
-    for h in (0, 29):
-        want = ox.block_sums(f(qkv["q"][:, h:h + 1]), f(qkv["k"][:, h:h + 1]), 8, 1.0, True)
+    say(f"  oracle block sums on {cfg.H} heads")
+    wants = parallel_map(lambda h: ox.block_sums(f(qkv["q"][:, h:h + 1]), f(qkv["k"][:, h:h + 1]),
+                                                 8, 1.0, True), range(cfg.H))
+    tol = 256 * (SUM_ATOL + SUM_RTOL * 8)
+    for h, want in enumerate(wants):
         np.testing.assert_allclose(sums[:, h:h + 1], want, rtol=SUM_RTOL, atol=SUM_ATOL)
-        tol = 256 * (SUM_ATOL + SUM_RTOL * 8)
         _check_valid_selection(mask[:, h:h + 1], want, 0.9, True, True, True, tol)
     # every head: rows add up to 8 reshaped rows, nothing after the diagonal
     np.testing.assert_allclose(sums.sum(axis=-1), 8.0, rtol=1e-5)
