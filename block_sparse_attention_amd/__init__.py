@@ -21,7 +21,8 @@ __all__ = [
     "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices", "bsattn_fwd_chunk",
     "bsattn_fwd_topk", "bsattn_fwd_threshold",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
-    "bsattn_decode_gqa", "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
+    "bsattn_decode_gqa", "bsattn_decode_gqa_noalloc", "bsattn_decode_noalloc_scratch_bytes",
+    "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
     "bsattn_xattn_workspace_bytes", "bsattn_xattn_block_sums", "bsattn_build_mask_cumulative",
     "bsattn_xattn_estimate", "EXPORTED_SYMBOLS",
 ]
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "bsattn_fwd_chunk",
     "bsattn_fwd_topk", "bsattn_fwd_threshold", "bsattn_xattn_workspace_bytes",
     "bsattn_xattn_block_sums", "bsattn_build_mask_cumulative", "bsattn_xattn_estimate",
+    "bsattn_decode_gqa_noalloc", "bsattn_decode_noalloc_scratch_bytes",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -72,6 +74,8 @@ _SIGS = {
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "bsattn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_decode_gqa_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_decode_noalloc_scratch_bytes": (_Z, []),
     "bsattn_decode_gqa_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_decode_gqa_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _P, _P, _Z, _P]),
@@ -400,6 +404,30 @@ def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0,
     _check("bsattn_decode_gqa", load_library().bsattn_decode_gqa(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
         max_sel, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def bsattn_decode_noalloc_scratch_bytes() -> int:
+    return int(load_library().bsattn_decode_noalloc_scratch_bytes())
+
+
+def bsattn_decode_gqa_noalloc(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0, out=None,
+                              stream=None):
+    """bsattn_decode_gqa whose split partials live in the library's static
+    scratch array (no workspace; the C call allocates nothing).  Calls that
+    overlap in time on one GPU share that array and must not overlap."""
+    torch = _torch()
+    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    _dev(block_indices, "block_indices", torch.int32, 3)
+    if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
+        raise ValueError("block_indices must be [B, Hkv, max_sel]")
+    max_sel = block_indices.shape[2]
+    if out is None:
+        out = _empty((B, Hq, D), torch.bfloat16, q.device, stream)
+    _dev(out, "out", torch.bfloat16, 3)
+    _check("bsattn_decode_gqa_noalloc", load_library().bsattn_decode_gqa_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
+        max_sel, total_k, int(num_splits), _ptr(out), _stream(stream)))
     return out
 
 

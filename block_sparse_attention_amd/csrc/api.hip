@@ -81,6 +81,36 @@ size_t decode_ws(int B, int Hq, int D, int ns) {
   return align_up(parts * D * sizeof(float)) + align_up(parts * sizeof(float));
 }
 
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+
+}  // namespace
+
+// Scratch of the decode entry point that allocates nothing: the split
+// stage's partials live in this file-scope device array (one copy per GPU,
+// held until the process ends).  In host code `decode_scratch` names a
+// host-side stand-in, never the device memory; the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char decode_scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::atomic<void*> g_decode_scratch[64];
+
+// The device address of decode_scratch on the current device, or nullptr if
+// the runtime cannot give it.
+void* decode_scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < 64) {
+    void* p = g_decode_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch)) != hipSuccess) return nullptr;
+  if (dev < 64 && p) g_decode_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,7 +301,8 @@ namespace {
 // form-specific pointers and sizes, `slots` is the per-(batch, KV head) slot
 // count the splits divide (max_selected_blocks, or num_blocks of a mask).
 bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            size_t workspace_bytes, hipStream_t stream,
+                            bool static_scratch = false) {
   if (!a.q || !a.k || !a.v || !a.out) return BSATTN_ERR_NULL;
   if (a.B <= 0 || a.Hq <= 0 || a.Hkv <= 0 || slots <= 0) return BSATTN_ERR_SHAPE;
   if (a.Hq % a.Hkv != 0) return BSATTN_ERR_SHAPE;
@@ -284,6 +315,13 @@ bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* works
     if (ns <= 0) return BSATTN_ERR_HIP;
   }
   const size_t need = decode_ws(a.B, a.Hq, a.D, ns);
+  if (static_scratch && need > 0) {
+    // the no-allocation form: the partials go to the static scratch array
+    if (need > kNoAllocScratchBytes) return BSATTN_ERR_WORKSPACE;
+    workspace = decode_scratch_ptr();
+    if (!workspace) return BSATTN_ERR_HIP;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
   const size_t parts = (size_t)a.B * a.Hq * ns;
   a.o_part = (float*)workspace;
@@ -312,6 +350,23 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
   return decode_common(a, max_selected_blocks, num_splits, workspace, workspace_bytes,
                        as_hip(stream));
 }
+
+bsattn_status bsattn_decode_gqa_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const int32_t* cu_seqlens_k, const int32_t* block_indices,
+                                        int B, int Hq, int Hkv, int D, int max_selected_blocks,
+                                        int total_k, int num_splits, uint16_t* out,
+                                        bsattn_stream_t stream) {
+  if (!q || !k || !v || !out || !cu_seqlens_k || !block_indices) return BSATTN_ERR_NULL;
+  if (total_k <= 0) return BSATTN_ERR_SHAPE;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.mode = kDecodeIndices;
+  return decode_common(a, max_selected_blocks, num_splits, nullptr, 0, as_hip(stream), true);
+}
+
+size_t bsattn_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* cu_seqlens_k, const uint8_t* block_mask, int B,

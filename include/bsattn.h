@@ -3,17 +3,20 @@
  *
  * Plain C ABI.  Every tensor argument is a caller-owned, contiguous, row-major
  * DEVICE buffer; bfloat16 tensors are passed as their uint16 bit patterns.
- * The library never allocates device memory and never synchronises the
- * host: each call only enqueues kernels on `stream` (a hipStream_t; NULL =
+ * The library never allocates device memory (its one static array, the
+ * scratch of bsattn_decode_gqa_noalloc, is part of the loaded code object)
+ * and never synchronises the host: each call only enqueues kernels on `stream` (a hipStream_t; NULL =
  * the default stream).  Outputs are valid once the stream reaches the end of
  * the call.  Equal inputs give bitwise equal outputs (no atomics on any
  * value path).
  *
  * Host state: the only state kept between calls is per device and
  * write-once in effect — the device's compute-unit count (read on first use,
- * for the default decode split count and the forward's launch shape) and
- * the largest dynamic-LDS size each kernel has been granted.  Both are
- * atomics, so the library is safe to call from several host threads.
+ * for the default decode split count and the forward's launch shape), the
+ * largest dynamic-LDS size each kernel has been granted, and the address of
+ * the static scratch array of bsattn_decode_gqa_noalloc.  All are atomics,
+ * so the library is safe to call from several host threads (that scratch
+ * array itself is shared: see bsattn_decode_gqa_noalloc).
  *
  * Errors: all argument checks run on the host BEFORE any launch.  On an
  * error nothing is enqueued and no output is touched.  A launch failure
@@ -253,6 +256,31 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
                                 int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
                                 int num_splits, uint16_t* out, void* workspace,
                                 size_t workspace_bytes, bsattn_stream_t stream);
+
+/*
+ * bsattn_decode_gqa without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of bsattn_decode_gqa (same kernels; equal inputs and split count give
+ * bitwise-equal outputs).  The split stage's partials go to a static device
+ * array inside the library, bsattn_decode_noalloc_scratch_bytes() = 8 MiB,
+ * one copy per GPU, held until the process ends; its address is looked up
+ * once per device on the first call there.  A call whose split count needs
+ * more (bsattn_decode_workspace_bytes above 8 MiB) returns
+ * BSATTN_ERR_WORKSPACE and enqueues nothing.  Nothing in the scratch needs
+ * clearing: every split writes its partial and log-sum-exp before the merge
+ * reads them.  All calls on one GPU share the array, so calls that may
+ * overlap in time on one GPU (several streams, several host threads) race
+ * and must be serialised by the caller.  The call itself allocates nothing.
+ */
+bsattn_status bsattn_decode_gqa_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const int32_t* cu_seqlens_k, const int32_t* block_indices,
+                                        int B, int Hq, int Hkv, int D, int max_selected_blocks,
+                                        int total_k, int num_splits, uint16_t* out,
+                                        bsattn_stream_t stream);
+
+/* Size of the static scratch array of bsattn_decode_gqa_noalloc (8 MiB). */
+size_t bsattn_decode_noalloc_scratch_bytes(void);
 
 /*
  * Mask-form sparse GQA decode (same guide, §6: the variant of the varlen

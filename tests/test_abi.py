@@ -111,6 +111,25 @@ def test_decode_validates_on_host():
     assert lib.bsattn_decode_workspace_bytes(0, 8, 128, 2) == 0
 
 
+def test_noalloc_decode_validates_on_host():
+    lib = _lib()
+    F = FAKE
+
+    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2):
+        return lib.bsattn_decode_gqa_noalloc(q, F, F, cu, F, B, Hq, Hkv, D, ms, tk, ns, F, None)
+
+    assert lib.bsattn_decode_noalloc_scratch_bytes() == 8 << 20
+    assert call(q=None) == 1
+    assert call(cu=None) == 1
+    assert call(Hq=6, Hkv=4) == 2
+    assert call(ns=5) == 2
+    assert call(tk=0) == 2
+    assert call(D=80) == 3
+    # partials beyond the 8 MiB scratch array are refused before any device call
+    assert lib.bsattn_decode_workspace_bytes(64, 64, 128, 64) > 8 << 20
+    assert call(B=64, Hq=64, Hkv=4, ms=64, ns=64) == 4
+
+
 def test_fused_fwd_validates_on_host():
     lib = _lib()
     F = FAKE
