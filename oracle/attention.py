@@ -114,13 +114,16 @@ def decode_allowed_tokens(len_b: int, indices: Iterable[int]) -> np.ndarray:
 
 def decode_gqa(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_k: np.ndarray,
                block_indices: np.ndarray) -> np.ndarray:
-    """q float64 [B, Hq, D]; k, v float64 [total_k, Hkv, D]; cu_seqlens_k [B+1];
-    block_indices [B, Hkv, max_sel] -> float64 [B, Hq, D]."""
+    """q float64 [B, Hq, D]; k float64 [total_k, Hkv, D]; v float64
+    [total_k, Hkv, Dv]; cu_seqlens_k [B+1]; block_indices [B, Hkv, max_sel]
+    -> float64 [B, Hq, Dv].  The value head dim Dv may differ from the key
+    head dim D (the guide's decode takes dim and dim_v, §9.2; the scores
+    scale by D^-1/2)."""
     B, Hq, D = q.shape
     Hkv = k.shape[1]
     assert Hq % Hkv == 0
     G = Hq // Hkv
-    out = np.zeros((B, Hq, D), dtype=np.float64)
+    out = np.zeros((B, Hq, v.shape[-1]), dtype=np.float64)
     for b in range(B):
         start, end = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
         for hq in range(Hq):
@@ -151,13 +154,14 @@ def decode_gqa_mask(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_k: n
     kvh when block_mask[b, kvh, j] != 0 and j < ceil(len_b / 64); everything
     else is as in ``decode_gqa``.
 
-    q float64 [B, Hq, D]; k, v float64 [total_k, Hkv, D]; cu_seqlens_k [B+1];
-    block_mask [B, Hkv, num_blocks] (nonzero = selected) -> float64 [B, Hq, D]."""
+    q float64 [B, Hq, D]; k float64 [total_k, Hkv, D]; v float64
+    [total_k, Hkv, Dv]; cu_seqlens_k [B+1]; block_mask [B, Hkv, num_blocks]
+    (nonzero = selected) -> float64 [B, Hq, Dv]."""
     B, Hq, D = q.shape
     Hkv = k.shape[1]
     assert Hq % Hkv == 0
     G = Hq // Hkv
-    out = np.zeros((B, Hq, D), dtype=np.float64)
+    out = np.zeros((B, Hq, v.shape[-1]), dtype=np.float64)
     for b in range(B):
         start, end = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
         for hq in range(Hq):
@@ -174,21 +178,21 @@ def decode_gqa_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                      block_indices: np.ndarray) -> np.ndarray:
     """Paged-KV sparse GQA decode (same guide, §7).
 
-    k_cache, v_cache float64 [num_pages, page_size, Hkv, D] with page_size a
-    multiple of 64; block_table [B, max_blocks_per_seq] maps a sequence's
+    k_cache float64 [num_pages, page_size, Hkv, D] and v_cache float64
+    [num_pages, page_size, Hkv, Dv] with page_size a multiple of 64; block_table [B, max_blocks_per_seq] maps a sequence's
     logical page to a physical page; cache_seqlens [B] are the lengths.
     Logical 64-token block i of sequence b is rows (i % r) * 64 .. +63 of
     physical page block_table[b, i // r], r = page_size // 64, so token t
     sits at row t % page_size of page block_table[b, t // page_size].  An
     index selects nothing when it is < 0, >= ceil(len_b / 64), or its table
     entry is missing or outside [0, num_pages) (the memory-safe reading).
-    Everything else is as in ``decode_gqa``.  -> float64 [B, Hq, D]."""
+    Everything else is as in ``decode_gqa``.  -> float64 [B, Hq, Dv]."""
     B, Hq, D = q.shape
     num_pages, page_size, Hkv, _ = k_cache.shape
     assert Hq % Hkv == 0 and page_size % BLOCK == 0
     G = Hq // Hkv
     r = page_size // BLOCK
-    out = np.zeros((B, Hq, D), dtype=np.float64)
+    out = np.zeros((B, Hq, v_cache.shape[-1]), dtype=np.float64)
     for b in range(B):
         len_b = int(cache_seqlens[b])
         for hq in range(Hq):
