@@ -73,11 +73,11 @@ _SIGS = {
     "bsattn_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
-    "bsattn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
-    "bsattn_decode_gqa_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "bsattn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_decode_gqa_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "bsattn_decode_noalloc_scratch_bytes": (_Z, []),
-    "bsattn_decode_gqa_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
-    "bsattn_decode_gqa_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+    "bsattn_decode_gqa_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "bsattn_decode_gqa_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _P, _P, _Z, _P]),
     "bsattn_xattn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "bsattn_xattn_block_sums": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _Z, _P]),
@@ -355,7 +355,7 @@ def bsattn_decode_workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> i
     return int(load_library().bsattn_decode_workspace_bytes(B, Hq, D, num_splits))
 
 
-def _decode_common(q, Hkv, slots, num_splits, out, workspace, stream):
+def _decode_common(q, Hkv, Dv, slots, num_splits, out, workspace, stream):
     torch = _torch()
     B, Hq, D = q.shape
     ns = int(num_splits)
@@ -364,9 +364,11 @@ def _decode_common(q, Hkv, slots, num_splits, out, workspace, stream):
         if ns <= 0:
             raise BsattnError("bsattn_decode_default_splits", 5, "could not query the device")
     if out is None:
-        out = _empty((B, Hq, D), torch.bfloat16, q.device, stream)
+        out = _empty((B, Hq, Dv), torch.bfloat16, q.device, stream)
     _dev(out, "out", torch.bfloat16, 3)
-    need = bsattn_decode_workspace_bytes(B, Hq, D, ns)
+    if tuple(out.shape) != (B, Hq, Dv):
+        raise ValueError(f"out must be [{B}, {Hq}, {Dv}]")
+    need = bsattn_decode_workspace_bytes(B, Hq, Dv, ns)
     ws_ptr, ws_bytes = 0, 0
     if need:
         if workspace is None:
@@ -383,11 +385,11 @@ def _decode_packed_checks(q, k, v, cu_seqlens_k):
     _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
     B, Hq, D = q.shape
     total_k, Hkv, Dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Dk != D:
-        raise ValueError("k and v must be [total_k, Hkv, D] with the query's D")
+    if Dk != D or v.shape[0] != total_k or v.shape[1] != Hkv:
+        raise ValueError("k must be [total_k, Hkv, D] with the query's D and v [total_k, Hkv, Dv]")
     if cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_k must be [B+1]")
-    return B, Hq, Hkv, D, total_k
+    return B, Hq, Hkv, D, v.shape[2], total_k
 
 
 def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0, out=None,
@@ -395,14 +397,14 @@ def bsattn_decode_gqa(q, k, v, cu_seqlens_k, block_indices, num_splits: int = 0,
     """Split-KV sparse GQA decode (guide §6).  q bf16 [B,Hq,D]; k,v bf16 [total_k,Hkv,D];
     cu_seqlens_k int32 [B+1]; block_indices int32 [B,Hkv,max_sel] (-1 = empty)."""
     torch = _torch()
-    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    B, Hq, Hkv, D, Dv, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
     _dev(block_indices, "block_indices", torch.int32, 3)
     if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
         raise ValueError("block_indices must be [B, Hkv, max_sel]")
     max_sel = block_indices.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace, stream)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, Dv, max_sel, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa", load_library().bsattn_decode_gqa(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D, Dv,
         max_sel, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out
 
@@ -417,16 +419,18 @@ def bsattn_decode_gqa_noalloc(q, k, v, cu_seqlens_k, block_indices, num_splits: 
     scratch array (no workspace; the C call allocates nothing).  Calls that
     overlap in time on one GPU share that array and must not overlap."""
     torch = _torch()
-    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    B, Hq, Hkv, D, Dv, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
     _dev(block_indices, "block_indices", torch.int32, 3)
     if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
         raise ValueError("block_indices must be [B, Hkv, max_sel]")
     max_sel = block_indices.shape[2]
     if out is None:
-        out = _empty((B, Hq, D), torch.bfloat16, q.device, stream)
+        out = _empty((B, Hq, Dv), torch.bfloat16, q.device, stream)
     _dev(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (B, Hq, Dv):
+        raise ValueError(f"out must be [{B}, {Hq}, {Dv}]")
     _check("bsattn_decode_gqa_noalloc", load_library().bsattn_decode_gqa_noalloc(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_indices), B, Hq, Hkv, D, Dv,
         max_sel, total_k, int(num_splits), _ptr(out), _stream(stream)))
     return out
 
@@ -436,16 +440,16 @@ def bsattn_decode_gqa_mask(q, k, v, cu_seqlens_k, block_mask, num_splits: int = 
     """Mask-form sparse GQA decode (guide §6).  As bsattn_decode_gqa, with
     block_mask uint8/bool [B,Hkv,num_blocks] (nonzero = block selected)."""
     torch = _torch()
-    B, Hq, Hkv, D, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
+    B, Hq, Hkv, D, Dv, total_k = _decode_packed_checks(q, k, v, cu_seqlens_k)
     if block_mask.dtype == torch.bool:
         block_mask = block_mask.view(torch.uint8)
     _dev(block_mask, "block_mask", torch.uint8, 3)
     if block_mask.shape[0] != B or block_mask.shape[1] != Hkv:
         raise ValueError("block_mask must be [B, Hkv, num_blocks]")
     nblocks = block_mask.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, nblocks, num_splits, out, workspace, stream)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, Dv, nblocks, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa_mask", load_library().bsattn_decode_gqa_mask(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_mask), B, Hq, Hkv, D,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), _ptr(block_mask), B, Hq, Hkv, D, Dv,
         nblocks, total_k, ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out
 
@@ -464,17 +468,19 @@ def bsattn_decode_gqa_paged(q, k_cache, v_cache, cache_seqlens, block_table, blo
     _dev(block_indices, "block_indices", torch.int32, 3)
     B, Hq, D = q.shape
     num_pages, page_size, Hkv, Dk = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D:
-        raise ValueError("k_cache and v_cache must be [num_pages, page_size, Hkv, D]")
+    if tuple(v_cache.shape[:3]) != tuple(k_cache.shape[:3]) or Dk != D:
+        raise ValueError("k_cache must be [num_pages, page_size, Hkv, D] and v_cache "
+                         "[num_pages, page_size, Hkv, Dv]")
+    Dv = v_cache.shape[3]
     if cache_seqlens.numel() != B or block_table.shape[0] != B:
         raise ValueError("cache_seqlens must be [B] and block_table [B, max_blocks_per_seq]")
     if block_indices.shape[0] != B or block_indices.shape[1] != Hkv:
         raise ValueError("block_indices must be [B, Hkv, max_sel]")
     max_sel = block_indices.shape[2]
-    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, max_sel, num_splits, out, workspace, stream)
+    ns, out, ws_ptr, ws_bytes = _decode_common(q, Hkv, Dv, max_sel, num_splits, out, workspace, stream)
     _check("bsattn_decode_gqa_paged", load_library().bsattn_decode_gqa_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
-        _ptr(block_indices), B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1], max_sel,
+        _ptr(block_indices), B, Hq, Hkv, D, Dv, num_pages, page_size, block_table.shape[1], max_sel,
         ns, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out
 

@@ -83,6 +83,9 @@ size_t decode_ws(int B, int Hq, int D, int ns) {
 
 constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
 
+// Query heads per KV head the decode takes (the guide's §6.1 block_H = 64).
+constexpr int kMaxDecodeGroup = 64;
+
 }  // namespace
 
 // Scratch of the decode entry point that allocates nothing: the split
@@ -120,7 +123,7 @@ const char* bsattn_status_string(bsattn_status s) {
     case BSATTN_OK: return "ok";
     case BSATTN_ERR_NULL: return "null pointer argument";
     case BSATTN_ERR_SHAPE: return "size out of range or inconsistent";
-    case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; decode group size <= 16)";
+    case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dims must be 64 or 128; decode group size <= 64)";
     case BSATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case BSATTN_ERR_HIP: return "HIP runtime error at launch";
   }
@@ -307,14 +310,16 @@ bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* works
   if (a.B <= 0 || a.Hq <= 0 || a.Hkv <= 0 || slots <= 0) return BSATTN_ERR_SHAPE;
   if (a.Hq % a.Hkv != 0) return BSATTN_ERR_SHAPE;
   if (num_splits > slots) return BSATTN_ERR_SHAPE;
-  if (!head_dim_ok(a.D) || a.Hq / a.Hkv > 16) return BSATTN_ERR_UNSUPPORTED;
-  if (a.B > 65535 || a.Hkv > 65535) return BSATTN_ERR_SHAPE;
+  if (!head_dim_ok(a.D) || !head_dim_ok(a.Dv) || a.Hq / a.Hkv > kMaxDecodeGroup)
+    return BSATTN_ERR_UNSUPPORTED;
+  // grid: splits x (KV heads x 16-head column tiles) x batch
+  if (a.B > 65535 || (long long)a.Hkv * ((a.Hq / a.Hkv + 15) / 16) > 65535) return BSATTN_ERR_SHAPE;
   int ns = num_splits;
   if (ns <= 0) {
     ns = bsattn_decode_default_splits(a.B, a.Hq, a.Hkv, slots, a.D);
     if (ns <= 0) return BSATTN_ERR_HIP;
   }
-  const size_t need = decode_ws(a.B, a.Hq, a.D, ns);
+  const size_t need = decode_ws(a.B, a.Hq, a.Dv, ns);
   if (static_scratch && need > 0) {
     // the no-allocation form: the partials go to the static scratch array
     if (need > kNoAllocScratchBytes) return BSATTN_ERR_WORKSPACE;
@@ -325,7 +330,7 @@ bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* works
   if (need > 0 && (!workspace || workspace_bytes < need)) return BSATTN_ERR_WORKSPACE;
   const size_t parts = (size_t)a.B * a.Hq * ns;
   a.o_part = (float*)workspace;
-  a.lse = need ? (float*)((char*)workspace + align_up(parts * a.D * sizeof(float))) : nullptr;
+  a.lse = need ? (float*)((char*)workspace + align_up(parts * a.Dv * sizeof(float))) : nullptr;
   a.max_sel = slots;
   a.num_splits = ns;
   return launch_decode(a, stream) == hipSuccess ? BSATTN_OK : BSATTN_ERR_HIP;
@@ -337,7 +342,7 @@ extern "C" {
 
 bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* cu_seqlens_k, const int32_t* block_indices, int B,
-                                int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
+                                int Hq, int Hkv, int D, int Dv, int max_selected_blocks, int total_k,
                                 int num_splits, uint16_t* out, void* workspace,
                                 size_t workspace_bytes, bsattn_stream_t stream) {
   if (!q || !k || !v || !out || !cu_seqlens_k || !block_indices) return BSATTN_ERR_NULL;
@@ -345,7 +350,7 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.Dv = Dv; a.total_k = total_k;
   a.mode = kDecodeIndices;
   return decode_common(a, max_selected_blocks, num_splits, workspace, workspace_bytes,
                        as_hip(stream));
@@ -353,7 +358,7 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
 
 bsattn_status bsattn_decode_gqa_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const int32_t* cu_seqlens_k, const int32_t* block_indices,
-                                        int B, int Hq, int Hkv, int D, int max_selected_blocks,
+                                        int B, int Hq, int Hkv, int D, int Dv, int max_selected_blocks,
                                         int total_k, int num_splits, uint16_t* out,
                                         bsattn_stream_t stream) {
   if (!q || !k || !v || !out || !cu_seqlens_k || !block_indices) return BSATTN_ERR_NULL;
@@ -361,7 +366,7 @@ bsattn_status bsattn_decode_gqa_noalloc(const uint16_t* q, const uint16_t* k, co
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.cu_seqlens = cu_seqlens_k; a.block_indices = block_indices;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.Dv = Dv; a.total_k = total_k;
   a.mode = kDecodeIndices;
   return decode_common(a, max_selected_blocks, num_splits, nullptr, 0, as_hip(stream), true);
 }
@@ -370,7 +375,7 @@ size_t bsattn_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; 
 
 bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* cu_seqlens_k, const uint8_t* block_mask, int B,
-                                     int Hq, int Hkv, int D, int num_blocks, int total_k,
+                                     int Hq, int Hkv, int D, int Dv, int num_blocks, int total_k,
                                      int num_splits, uint16_t* out, void* workspace,
                                      size_t workspace_bytes, bsattn_stream_t stream) {
   if (!q || !k || !v || !out || !cu_seqlens_k || !block_mask) return BSATTN_ERR_NULL;
@@ -378,7 +383,7 @@ bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.cu_seqlens = cu_seqlens_k; a.block_mask = block_mask;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.total_k = total_k;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.Dv = Dv; a.total_k = total_k;
   a.mode = kDecodeMask;
   return decode_common(a, num_blocks, num_splits, workspace, workspace_bytes, as_hip(stream));
 }
@@ -386,7 +391,7 @@ bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const
 bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache,
                                       const uint16_t* v_cache, const int32_t* cache_seqlens,
                                       const int32_t* block_table, const int32_t* block_indices,
-                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int B, int Hq, int Hkv, int D, int Dv, int num_pages, int page_size,
                                       int max_blocks_per_seq, int max_selected_blocks,
                                       int num_splits, uint16_t* out, void* workspace,
                                       size_t workspace_bytes, bsattn_stream_t stream) {
@@ -394,12 +399,12 @@ bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache
     return BSATTN_ERR_NULL;
   if (num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0) return BSATTN_ERR_SHAPE;
   if (page_size % BSATTN_BLOCK != 0) return BSATTN_ERR_SHAPE;
-  if (!fits_elems((long double)num_pages * page_size * (Hkv > 0 ? Hkv : 1) * 128))
+  if (!fits_elems((long double)num_pages * page_size * (Hkv > 0 ? Hkv : 1) * 128 * 2))
     return BSATTN_ERR_SHAPE;
   DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
   a.cache_seqlens = cache_seqlens; a.block_table = block_table; a.block_indices = block_indices;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.Dv = Dv;
   a.num_pages = num_pages; a.page_size = page_size; a.max_blocks_per_seq = max_blocks_per_seq;
   a.mode = kDecodePaged;
   return decode_common(a, max_selected_blocks, num_splits, workspace, workspace_bytes,

@@ -7,15 +7,18 @@
 // beyond the sequence length are masked; each range produces a normalised
 // partial output and its base-2 log-sum-exp, and a merge kernel combines the
 // ranges with weights 2^(lse - max lse) (§6.1).  Query head hq reads KV head
-// hq / (Hq / Hkv).
+// hq / (Hq / Hkv); up to 64 query heads share a KV head (§6.1: valid_block_H =
+// min(64, group)).  V's head dim may differ from K's (§9.2: dim and dim_v).
 //
 // CDNA4 mapping (not the guide's kernel design):
-// * one work-group of 8 wave64s per (batch, KV head, split), two waves per
-//   SIMD; the waves take the range's slots round-robin and are combined
-//   through LDS at the end;
-// * per 64-token block, S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
-//   group's query heads as the 16 columns (K rows loaded straight from HBM
-//   into the A-operand layout, 16 bytes per lane);
+// * one work-group of 8 wave64s per (batch, KV head, split, 16-head column
+//   tile), two waves per SIMD; the waves take the range's slots round-robin
+//   and are combined through LDS at the end;
+// * per 64-token block, S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 with 16 of
+//   the group's query heads as the columns (K rows loaded straight from HBM
+//   into the A-operand layout, 16 bytes per lane); groups of more than 16
+//   heads take one work-group per 16-head tile, whose K/V reads of the same
+//   blocks meet in the caches;
 // * the exponentiated scores are already the B operand of O^T = V^T . P^T;
 //   V goes through LDS, read transposed with ds_read_b64_tr_b16;
 // * software pipeline per wave: the next selected block's K loads are issued
@@ -70,26 +73,28 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-template <int D>
+// D: key/query head dim; DV: value (and output) head dim.
+template <int D, int DV>
 struct DCfg {
-  static constexpr int kStride = D + 16;     // LDS row stride of a V half tile
+  static constexpr int kStride = DV + 16;    // LDS row stride of a V half tile
   static constexpr int kSteps = D / 32;      // k-steps of S^T = K . Q^T
-  static constexpr int kDT = D / 16;         // 16-row tiles of O^T
-  static constexpr int kRowChunks = D / 8;   // 16-byte chunks per token row
+  static constexpr int kDT = DV / 16;        // 16-row tiles of O^T
+  static constexpr int kRowChunks = DV / 8;  // 16-byte chunks per V token row
   static constexpr int kVPer = 64 * kRowChunks / kWave;  // V chunks per lane per block
   static constexpr int kTokPerInstr = kWave / kRowChunks;  // V tokens per load instruction
-  static constexpr int kWaveLds = 32 * kStride;          // bf16 elements per wave
-  // the combine reuses a wave's region as floats: 16 m, 16 l, 16 x D o
-  static_assert(kWaveLds * 2 >= (32 + 16 * D) * 4, "combine area");
+  // bf16 elements per wave: the V half tile, or the combine's floats
+  // (16 m, 16 l, 16 x DV o), whichever is larger
+  static constexpr int kWaveLds =
+      32 * kStride > (32 + 16 * DV) * 2 ? 32 * kStride : (32 + 16 * DV) * 2;
 };
 
 template <int D>
 struct KTile {
   u32x4 f[4][D / 32];
 };
-template <int D>
+template <int D, int DV>
 struct VTile {
-  u32x4 f[DCfg<D>::kVPer];
+  u32x4 f[DCfg<D, DV>::kVPer];
 };
 
 // Position of the r-th (from 0) set bit of x; x has more than r set bits.
@@ -113,16 +118,19 @@ struct BlockRef {
   int page;
 };
 
-template <int D, int MODE>
+template <int D, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int final_out) {
-  using C = DCfg<D>;
+  using C = DCfg<D, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * C::kWaveLds];
 
   const int sid = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int G = a.Hq / a.Hkv;
+  const int nct = (G + 15) / 16;                      // 16-head column tiles per KV head
+  const int kvh = (int)blockIdx.y / nct;
+  const int col0 = 16 * ((int)blockIdx.y - kvh * nct);  // first group head of this tile
+  const int Gt = min(16, G - col0);                   // heads in this tile
   const int b = blockIdx.z;
   const int ns = a.num_splits;
-  const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -184,16 +192,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   }
   const int nper = my_len > w ? (my_len - w + kWaves - 1) / kWaves : 0;
 
-  const uint32_t rsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens
+  const uint32_t rsb = (uint32_t)a.Hkv * D * 2;    // bytes between consecutive K tokens
+  const uint32_t rsbv = (uint32_t)a.Hkv * DV * 2;  // bytes between consecutive V tokens
   const float c = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
 
-  // Q^T as the B operand: column col = query head kvh*G + col (zero when col >= G).
+  // Q^T as the B operand: column col = query head kvh*G + col0 + col (zero when col >= Gt).
   u32x4 qf[C::kSteps];
   {
-    const int hq = kvh * G + col;
+    const int hq = kvh * G + col0 + col;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
-      if (col < G)
+      if (col < Gt)
         qf[s] = *(const u32x4*)(a.q + ((int64_t)b * a.Hq + hq) * D + 32 * s + 8 * grp);
       else
         qf[s] = u32x4{0, 0, 0, 0};
@@ -214,27 +223,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   uint32_t koff[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) koff[tt] = (uint32_t)(16 * tt + col) * rsb + 16u * grp;
-  const uint32_t voff0 = (uint32_t)(lane / C::kRowChunks) * rsb + 16u * (lane % C::kRowChunks);
-  const uint32_t vstep = (uint32_t)C::kTokPerInstr * rsb;
+  const uint32_t voff0 = (uint32_t)(lane / C::kRowChunks) * rsbv + 16u * (lane % C::kRowChunks);
+  const uint32_t vstep = (uint32_t)C::kTokPerInstr * rsbv;
 
   // first row of a block: packed, row start + 64 blk; paged, row (blk % ratio) * 64 of its page
-  auto rsrc = [&](const uint16_t* p, BlockRef ref) {
+  // (tokens rs bytes apart, rows of hd elements)
+  auto rsrc = [&](const uint16_t* p, BlockRef ref, uint32_t rs, int hd) {
     const int ntok = min(64, len - ref.blk * 64);
     const int64_t row = MODE == kDecodePaged
                             ? (int64_t)ref.page * a.page_size + (int64_t)(ref.blk % ratio) * 64
                             : (int64_t)start + (int64_t)ref.blk * 64;
-    const uint16_t* base = p + row * (rsb / 2) + (int64_t)kvh * D;
-    return block_rsrc(base, (uint32_t)(ntok - 1) * rsb + D * 2);
+    const uint16_t* base = p + row * (rs / 2) + (int64_t)kvh * hd;
+    return block_rsrc(base, (uint32_t)(ntok - 1) * rs + hd * 2);
   };
   auto load_k = [&](BlockRef blk, KTile<D>& kt) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.k, blk);
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.k, blk, rsb, D);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) kt.f[tt][s] = bload16(r, koff[tt], 64u * s);
   };
-  auto load_v = [&](BlockRef blk, VTile<D>& vt) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.v, blk);
+  auto load_v = [&](BlockRef blk, VTile<D, DV>& vt) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.v, blk, rsbv, DV);
     // recomputed per block (not hoisted): one offset register instead of kVPer
     uint32_t vo = voff0;
     asm volatile("" : "+v"(vo));
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 
   // one selected block: S^T, softmax, O^T += V^T . P^T; with MORE, the next
   // block's K loads go out after S^T and its V loads after P.V
-  auto process = [&](BlockRef blk, BlockRef nblk, KTile<D>& kt, VTile<D>& vt, auto more_c) {
+  auto process = [&](BlockRef blk, BlockRef nblk, KTile<D>& kt, VTile<D, DV>& vt, auto more_c) {
     constexpr bool kMore = decltype(more_c)::value;
     const int ntok = min(64, len - blk.blk * 64);
     // S^T tiles: token 16*tt + 4*grp + r, query column col
@@ -362,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
       return BlockRef{__builtin_amdgcn_readlane(bv, j), __builtin_amdgcn_readlane(pg, j)};
     };
     KTile<D> kt;
-    VTile<D> vt;
+    VTile<D, DV> vt;
     BlockRef blk = take();
     load_k(blk, kt);
     load_v(blk, vt);
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   l += __shfl_xor(l, 32);
   wave_lds_sync();
   __syncthreads();
-  float* red = (float*)(lds + w * C::kWaveLds);   // [16 m][16 l][16 * D o]
+  float* red = (float*)(lds + w * C::kWaveLds);   // [16 m][16 l][16 * DV o]
   if (grp == 0) {
     red[col] = m;
     red[16 + col] = l;
@@ -387,12 +397,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 #pragma unroll
   for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[32 + col * D + 16 * t + 4 * grp + r] = o[t][r];
+    for (int r = 0; r < 4; ++r) red[32 + col * DV + 16 * t + 4 * grp + r] = o[t][r];
   __syncthreads();
 
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int qn = e / D;
-    const int d = e - qn * D;
+  for (int e = tid; e < Gt * DV; e += kThreads) {
+    const int qn = e / DV;
+    const int d = e - qn * DV;
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ((float*)(lds + ww * C::kWaveLds))[qn]);
@@ -404,16 +414,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
         const float mw = rw[qn];
         const float wt = (mw == -INFINITY) ? 0.0f : fast_exp2((mw - M) * c);
         L += rw[16 + qn] * wt;
-        acc += rw[32 + qn * D + d] * wt;
+        acc += rw[32 + qn * DV + d] * wt;
       }
     }
     const float val = L > 0.0f ? acc / L : 0.0f;
-    const int hq = kvh * G + qn;
+    const int hq = kvh * G + col0 + qn;
     if (final_out) {
-      a.out[((int64_t)b * a.Hq + hq) * D + d] = float_to_bf16_bits(val);
+      a.out[((int64_t)b * a.Hq + hq) * DV + d] = float_to_bf16_bits(val);
     } else {
       const int64_t pi = ((int64_t)b * a.Hq + hq) * ns + sid;
-      a.o_part[pi * D + d] = val;
+      a.o_part[pi * DV + d] = val;
       if (d == 0) a.lse[pi] = L > 0.0f ? M * c + __log2f(L) : -INFINITY;
     }
   }
@@ -448,14 +458,15 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   a.out[bq * D + d] = float_to_bf16_bits(den > 0.0f ? num / den : 0.0f);
 }
 
-template <int D, int MODE>
+template <int D, int DV, int MODE>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int final_out = a.num_splits == 1 ? 1 : 0;
-  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.num_splits, a.Hkv, a.B), dim3(kThreads),
-                     0, stream, a, final_out);
+  const int nct = (a.Hq / a.Hkv + 15) / 16;
+  hipLaunchKernelGGL((decode_split_kernel<D, DV, MODE>), dim3(a.num_splits, a.Hkv * nct, a.B),
+                     dim3(kThreads), 0, stream, a, final_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || final_out) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(D), 0,
+  hipLaunchKernelGGL(decode_merge_kernel<DV>, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(DV), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -463,7 +474,8 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 template <int MODE>
 hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
-  return a.D == 64 ? launch_t<64, MODE>(a, stream) : launch_t<128, MODE>(a, stream);
+  if (a.D == 64) return a.Dv == 64 ? launch_t<64, 64, MODE>(a, stream) : launch_t<64, 128, MODE>(a, stream);
+  return a.Dv == 64 ? launch_t<128, 64, MODE>(a, stream) : launch_t<128, 128, MODE>(a, stream);
 }
 
 }  // namespace

@@ -114,16 +114,16 @@ enum DecodeMode {
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k;               // packed [total_k, Hkv, D] or paged [num_pages, page_size, Hkv, D]
-  const uint16_t* v;
+  const uint16_t* v;               // as k, with Dv in place of D
   const int32_t* cu_seqlens;       // packed modes
   const int32_t* block_indices;    // index and paged modes
   const uint8_t* block_mask;       // mask mode
   const int32_t* cache_seqlens;    // paged mode
   const int32_t* block_table;      // paged mode: [B, max_blocks_per_seq]
-  uint16_t* out;
-  float* o_part;   // [B, Hq, ns, D]
+  uint16_t* out;   // [B, Hq, Dv]
+  float* o_part;   // [B, Hq, ns, Dv]
   float* lse;      // [B, Hq, ns]
-  int B, Hq, Hkv, D, max_sel, total_k, num_splits;
+  int B, Hq, Hkv, D, Dv, max_sel, total_k, num_splits;   // D: q/k head dim, Dv: v/out head dim
   int page_size, num_pages, max_blocks_per_seq;
   int mode;
 };

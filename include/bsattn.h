@@ -213,32 +213,39 @@ bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint1
  * max_selected_blocks); one split when the m-blocks already fill 80% of the
  * machine or there are at most 4 blocks).  One (batch, KV head) pair is one
  * m-block.  Returns a value >= 1, or 0 when an argument is out of range.
+ * The guide sizes a KV head as blocks * 64 * (dim + dim_v) * 2 bytes for its
+ * branch that splits m-blocks larger than the L2; that branch needs two
+ * m-blocks per compute unit per (batch, KV head), which decode never has, so
+ * the value head dim does not enter and D stands for both.
  */
 int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, int D,
                              int num_cus);
 
 /* Workspace for bsattn_decode_gqa and its mask and paged forms: what the
  * split stage hands the merge stage (same guide, §6.1: one partial output
- * and one log-sum-exp per split) — fp32 partial outputs [B, Hq, splits, D]
- * and their base-2 log-sum-exp [B, Hq, splits], each part 256-byte aligned.
- * 0 when num_splits is 1 (the split kernel then writes out directly) or an
- * argument is out of range. */
-size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+ * and one log-sum-exp per split) — fp32 partial outputs [B, Hq, splits, Dv]
+ * and their base-2 log-sum-exp [B, Hq, splits], each part 256-byte aligned;
+ * Dv is the value head dim.  0 when num_splits is 1 (the split kernel then
+ * writes out directly) or an argument is out of range. */
+size_t bsattn_decode_workspace_bytes(int B, int Hq, int Dv, int num_splits);
 
 /*
  * Split-KV sparse GQA decode over packed variable-length KV (same guide,
  * §6, §6.1, §6.2), one query token per sequence.
  *   q            : bfloat16 [B, Hq, D]
- *   k, v         : bfloat16 [total_k, Hkv, D], sequence b occupies rows
+ *   k            : bfloat16 [total_k, Hkv, D], sequence b occupies rows
  *                  cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   v            : bfloat16 [total_k, Hkv, Dv] (Dv, the value head dim, may
+ *                  differ from D: the guide's dim_v, §9.2)
  *   cu_seqlens_k : int32 [B + 1], nondecreasing, cu[0] = 0, cu[B] <= total_k
  *   block_indices: int32 [B, Hkv, max_selected_blocks]; entry i selects
  *                  tokens [64 i, min(64 i + 64, len_b)) of the sequence; -1
  *                  (or any i < 0 or i >= ceil(len_b / 64)) selects nothing.
  *                  Order does not matter; duplicates are not allowed.
- *   out          : bfloat16 [B, Hq, D]
+ *   out          : bfloat16 [B, Hq, Dv]
  * Query head hq reads KV head hq / (Hq / Hkv) (consecutive query heads share
- * a KV head).  out = softmax(q . k_t / sqrt(D)) V over the selected tokens;
+ * a KV head; up to 64 per KV head, the guide's §6.1 block_H).
+ * out = softmax(q . k_t / sqrt(D)) V over the selected tokens;
  * zeros when nothing is selected.  The slot list of each (batch, KV head) is
  * cut into num_splits contiguous ranges (the first (slots mod splits) ranges
  * one slot longer); each range yields a partial output and a log-sum-exp,
@@ -247,14 +254,14 @@ size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  * A sequence whose cu_seqlens_k range is decreasing or ends beyond total_k
  * is treated as empty.
  * Errors: NULL pointers; B, Hq, Hkv, max_selected_blocks, total_k <= 0,
- * Hq % Hkv != 0, num_splits > max_selected_blocks (SHAPE); D not 64 or 128,
- * or Hq / Hkv > 16 (UNSUPPORTED); workspace smaller than
+ * Hq % Hkv != 0, num_splits > max_selected_blocks (SHAPE); D or Dv not 64 or
+ * 128, or Hq / Hkv > 64 (UNSUPPORTED); workspace smaller than
  * bsattn_decode_workspace_bytes for the split count used (WORKSPACE).
  */
 bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* cu_seqlens_k, const int32_t* block_indices, int B,
-                                int Hq, int Hkv, int D, int max_selected_blocks, int total_k,
-                                int num_splits, uint16_t* out, void* workspace,
+                                int Hq, int Hkv, int D, int Dv, int max_selected_blocks,
+                                int total_k, int num_splits, uint16_t* out, void* workspace,
                                 size_t workspace_bytes, bsattn_stream_t stream);
 
 /*
@@ -275,9 +282,9 @@ bsattn_status bsattn_decode_gqa(const uint16_t* q, const uint16_t* k, const uint
  */
 bsattn_status bsattn_decode_gqa_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const int32_t* cu_seqlens_k, const int32_t* block_indices,
-                                        int B, int Hq, int Hkv, int D, int max_selected_blocks,
-                                        int total_k, int num_splits, uint16_t* out,
-                                        bsattn_stream_t stream);
+                                        int B, int Hq, int Hkv, int D, int Dv,
+                                        int max_selected_blocks, int total_k, int num_splits,
+                                        uint16_t* out, bsattn_stream_t stream);
 
 /* Size of the static scratch array of bsattn_decode_gqa_noalloc (8 MiB). */
 size_t bsattn_decode_noalloc_scratch_bytes(void);
@@ -301,15 +308,16 @@ size_t bsattn_decode_noalloc_scratch_bytes(void);
  */
 bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* cu_seqlens_k, const uint8_t* block_mask, int B,
-                                     int Hq, int Hkv, int D, int num_blocks, int total_k,
+                                     int Hq, int Hkv, int D, int Dv, int num_blocks, int total_k,
                                      int num_splits, uint16_t* out, void* workspace,
                                      size_t workspace_bytes, bsattn_stream_t stream);
 
 /*
  * Paged-KV sparse GQA decode (same guide, §7: the index-form decode over a
  * page-organised KV cache, as kept by paged-attention serving engines).
- *   k_cache, v_cache : bfloat16 [num_pages, page_size, Hkv, D]; page_size a
+ *   k_cache          : bfloat16 [num_pages, page_size, Hkv, D]; page_size a
  *                      multiple of 64
+ *   v_cache          : bfloat16 [num_pages, page_size, Hkv, Dv]
  *   cache_seqlens    : int32 [B], sequence lengths (negative: empty)
  *   block_table      : int32 [B, max_blocks_per_seq]; logical page p of
  *                      sequence b is physical page block_table[b, p]
@@ -327,7 +335,8 @@ bsattn_status bsattn_decode_gqa_mask(const uint16_t* q, const uint16_t* k, const
 bsattn_status bsattn_decode_gqa_paged(const uint16_t* q, const uint16_t* k_cache,
                                       const uint16_t* v_cache, const int32_t* cache_seqlens,
                                       const int32_t* block_table, const int32_t* block_indices,
-                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int B, int Hq, int Hkv, int D, int Dv, int num_pages,
+                                      int page_size,
                                       int max_blocks_per_seq, int max_selected_blocks,
                                       int num_splits, uint16_t* out, void* workspace,
                                       size_t workspace_bytes, bsattn_stream_t stream);

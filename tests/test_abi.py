@@ -92,8 +92,8 @@ def test_decode_validates_on_host():
     F = FAKE
     args = dict(B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2)
 
-    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2, ws=None, wsb=0):
-        return lib.bsattn_decode_gqa(q, F, F, cu, F, B, Hq, Hkv, D, ms, tk, ns, F, ws, wsb, None)
+    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, Dv=128, ms=4, tk=100, ns=2, ws=None, wsb=0):
+        return lib.bsattn_decode_gqa(q, F, F, cu, F, B, Hq, Hkv, D, Dv, ms, tk, ns, F, ws, wsb, None)
 
     assert call(q=None) == 1
     assert call(cu=None) == 1
@@ -102,7 +102,10 @@ def test_decode_validates_on_host():
     assert call(ms=0) == 2
     assert call(tk=0) == 2
     assert call(D=80) == 3
-    assert call(Hq=34, Hkv=2) == 3         # group of 17 query heads
+    assert call(Dv=96) == 3
+    assert call(Hq=130, Hkv=2) == 3        # group of 65 query heads
+    assert call(Hq=128, Hkv=2, ns=2) == 4  # a group of 64 is taken; partials need a workspace
+    assert call(D=64, Dv=128, ns=2) == 4   # head dims may differ
     assert call(ns=2) == 4                 # partials need a workspace
     need = lib.bsattn_decode_workspace_bytes(2, 8, 128, 2)
     assert need >= 2 * 8 * 2 * (128 + 1) * 4 and need % 256 == 0
@@ -115,8 +118,8 @@ def test_noalloc_decode_validates_on_host():
     lib = _lib()
     F = FAKE
 
-    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, ms=4, tk=100, ns=2):
-        return lib.bsattn_decode_gqa_noalloc(q, F, F, cu, F, B, Hq, Hkv, D, ms, tk, ns, F, None)
+    def call(q=F, cu=F, B=2, Hq=8, Hkv=2, D=128, Dv=128, ms=4, tk=100, ns=2):
+        return lib.bsattn_decode_gqa_noalloc(q, F, F, cu, F, B, Hq, Hkv, D, Dv, ms, tk, ns, F, None)
 
     assert lib.bsattn_decode_noalloc_scratch_bytes() == 8 << 20
     assert call(q=None) == 1
@@ -191,8 +194,9 @@ def test_mask_form_decode_validates_on_host():
     lib = _lib()
     F = FAKE
 
-    def call(q=F, bm=F, B=2, Hq=8, Hkv=2, D=128, nbk=4, tk=100, ns=2, ws=None, wsb=0):
-        return lib.bsattn_decode_gqa_mask(q, F, F, F, bm, B, Hq, Hkv, D, nbk, tk, ns, F, ws, wsb, None)
+    def call(q=F, bm=F, B=2, Hq=8, Hkv=2, D=128, Dv=128, nbk=4, tk=100, ns=2, ws=None, wsb=0):
+        return lib.bsattn_decode_gqa_mask(q, F, F, F, bm, B, Hq, Hkv, D, Dv, nbk, tk, ns, F, ws, wsb,
+                                          None)
 
     assert call(q=None) == 1
     assert call(bm=None) == 1
@@ -201,6 +205,8 @@ def test_mask_form_decode_validates_on_host():
     assert call(tk=0) == 2
     assert call(Hq=6, Hkv=4) == 2
     assert call(D=96) == 3
+    assert call(Dv=32) == 3
+    assert call(Hq=130, Hkv=2) == 3
     assert call(ns=2) == 4
 
 
@@ -208,9 +214,10 @@ def test_paged_decode_validates_on_host():
     lib = _lib()
     F = FAKE
 
-    def call(q=F, tab=F, B=2, Hq=8, Hkv=2, D=128, npg=16, psz=256, mbps=4, ms=8, ns=2, ws=None, wsb=0):
-        return lib.bsattn_decode_gqa_paged(q, F, F, F, tab, F, B, Hq, Hkv, D, npg, psz, mbps, ms, ns,
-                                           F, ws, wsb, None)
+    def call(q=F, tab=F, B=2, Hq=8, Hkv=2, D=128, Dv=128, npg=16, psz=256, mbps=4, ms=8, ns=2,
+             ws=None, wsb=0):
+        return lib.bsattn_decode_gqa_paged(q, F, F, F, tab, F, B, Hq, Hkv, D, Dv, npg, psz, mbps, ms,
+                                           ns, F, ws, wsb, None)
 
     assert call(q=None) == 1
     assert call(tab=None) == 1
@@ -220,7 +227,8 @@ def test_paged_decode_validates_on_host():
     assert call(mbps=0) == 2
     assert call(ms=0) == 2
     assert call(ns=9) == 2
-    assert call(Hq=34, Hkv=2) == 3
+    assert call(Hq=130, Hkv=2) == 3
+    assert call(Dv=80) == 3
     assert call(ns=2) == 4
 
 
@@ -268,6 +276,8 @@ int main(void) {
   bad += bsattn_fwd(f16, f16, f16, m8, 1, 1, 64, 96, 1, (uint16_t*)f16, NULL, 0, NULL)
          != BSATTN_ERR_UNSUPPORTED;
   bad += bsattn_decode_num_splits(8, 32, 8, 64, 128, 256) != 4;
+  bad += bsattn_decode_gqa(f16, f16, f16, NULL, NULL, 8, 32, 8, 128, 64, 64, 100, 4,
+                           (uint16_t*)f16, NULL, 0, NULL) != BSATTN_ERR_NULL;
   printf("%s %s %d\n", bsattn_version(), bsattn_status_string(BSATTN_ERR_SHAPE), bad);
   return bad;
 }
