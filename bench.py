@@ -195,10 +195,12 @@ def bench_prefill(cfg_name: str, steps: int, warmup: int, flush=None, fused=True
         # the same path in one launch: row selection, compaction and forward
         if cfg.mask_kind == "topk":
             bsa.bsattn_fwd_topk(q, k, v, scores, cfg.topk, cfg.dense_last_two_rows,
-                                cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask)
+                                cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask,
+                                workspace=ws)
         else:
             bsa.bsattn_fwd_threshold(q, k, v, scores, cfg.threshold, cfg.dense_last_two_rows,
-                                     cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask)
+                                     cfg.force_diagonal, cfg.is_causal, out=out, mask_out=mask,
+                                     workspace=ws)
 
     _settle(step)
     for _ in range(warmup):

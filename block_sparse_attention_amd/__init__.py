@@ -68,8 +68,9 @@ _SIGS = {
     "bsattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_fwd_indices": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "bsattn_fwd_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
-    "bsattn_fwd_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
-    "bsattn_fwd_threshold": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P, _P]),
+    "bsattn_fwd_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "bsattn_fwd_threshold": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P, _P, _Z,
+                                  _P]),
     "bsattn_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "bsattn_decode_default_splits": (_I, [_I, _I, _I, _I, _I]),
     "bsattn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -240,16 +241,22 @@ def bsattn_fwd(q, k, v, block_mask, is_causal: bool = True, out=None, workspace=
     if out is None:
         out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
-    need = bsattn_fwd_workspace_bytes(B, H, S, D)
-    ws_ptr, ws_bytes = 0, 0
-    if need and (is_causal or workspace is not None):
-        if workspace is None:
-            workspace = _empty(need, torch.uint8, q.device, stream)
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _split_workspace(B, H, S, D, is_causal, workspace, q.device, stream)
     _check("bsattn_fwd", load_library().bsattn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), B, H, S, D, int(bool(is_causal)),
         _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return out
+
+
+def _split_workspace(B, H, S, D, is_causal, workspace, device, stream):
+    """(pointer, bytes) of the long-row split workspace: the caller's, or one
+    allocated for the call when the split needs one and none was given."""
+    need = bsattn_fwd_workspace_bytes(B, H, S, D)
+    if not need or not (is_causal or workspace is not None):
+        return 0, 0
+    if workspace is None:
+        workspace = _empty(need, _torch().uint8, device, stream)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stream=None):
@@ -292,27 +299,31 @@ def _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream):
 
 def bsattn_fwd_topk(q, k, v, scores, topk: int, dense_last_two_rows: bool = False,
                     force_diagonal: bool = True, is_causal: bool = True, out=None,
-                    mask_out=None, write_mask: bool = False, stream=None):
+                    mask_out=None, write_mask: bool = False, workspace=None, stream=None):
     """Top-k mask build + compaction + forward in one launch (guide §3.1, §4).
     The mask goes to mask_out when given (or to a new tensor with write_mask).
+    Long causal rows split as in bsattn_fwd (workspace as there).
     Returns out, or (out, mask) with write_mask."""
     B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream)
+    ws_ptr, ws_bytes = _split_workspace(B, H, S, D, is_causal, workspace, q.device, stream)
     _check("bsattn_fwd_topk", load_library().bsattn_fwd_topk(
         _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, int(topk),
         int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
-        _ptr(mask) if mask is not None else None, _ptr(out), _stream(stream)))
+        _ptr(mask) if mask is not None else None, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return (out, mask) if write_mask else out
 
 
 def bsattn_fwd_threshold(q, k, v, scores, threshold: float, dense_last_two_rows: bool = False,
                          force_diagonal: bool = True, is_causal: bool = True, out=None,
-                         mask_out=None, write_mask: bool = False, stream=None):
-    """Threshold mask build + compaction + forward in one launch (guide §3.2, §4)."""
+                         mask_out=None, write_mask: bool = False, workspace=None, stream=None):
+    """Threshold mask build + compaction + forward in one launch (guide §3.2, §4).
+    Long causal rows split as in bsattn_fwd (workspace as there)."""
     B, H, S, D, out, mask = _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream)
+    ws_ptr, ws_bytes = _split_workspace(B, H, S, D, is_causal, workspace, q.device, stream)
     _check("bsattn_fwd_threshold", load_library().bsattn_fwd_threshold(
         _ptr(q), _ptr(k), _ptr(v), _ptr(scores), B, H, S, D, float(threshold),
         int(bool(dense_last_two_rows)), int(bool(force_diagonal)), int(bool(is_causal)),
-        _ptr(mask) if mask is not None else None, _ptr(out), _stream(stream)))
+        _ptr(mask) if mask is not None else None, _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
     return (out, mask) if write_mask else out
 
 

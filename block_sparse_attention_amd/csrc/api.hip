@@ -201,6 +201,26 @@ static PrefillArgs fwd_args(const uint16_t* q, const uint16_t* k, const uint16_t
   return a;
 }
 
+// The long-row split of a causal square forward: checks the workspace and
+// points the split fields of `a` into it (nothing to do when no row can
+// exceed the split threshold).
+static bsattn_status set_long_row_split(PrefillArgs& a, int B, int H, int S, int D, int is_causal,
+                                        void* workspace, size_t workspace_bytes) {
+  if (B <= 0 || H <= 0 || S <= 0 || !head_dim_ok(D)) return BSATTN_OK;   // fwd_common reports it
+  const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
+  if (need == 0 || !is_causal) return BSATTN_OK;
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0)
+    return BSATTN_ERR_WORKSPACE;
+  const SplitLayout L = split_layout(B, H, nblocks(S), D);
+  unsigned char* ws = (unsigned char*)workspace;
+  a.split_min = kSplitMinBlocks;
+  a.split_row0 = kSplitMinBlocks;   // causal row i holds at most i + 1 blocks
+  a.part_o = (float*)(ws + L.o_off);
+  a.part_ml = (float2*)(ws + L.ml_off);
+  a.part_flag = (int*)(ws + L.flag_off);
+  return BSATTN_OK;
+}
+
 bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint8_t* block_mask, int B, int H, int S, int D, int is_causal,
                          uint16_t* out, void* workspace, size_t workspace_bytes,
@@ -208,20 +228,8 @@ bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
   if (!q || !k || !v || !block_mask || !out) return BSATTN_ERR_NULL;
   PrefillArgs a = fwd_args(q, k, v, out, kSrcMask);
   a.mask = block_mask;
-  if (B > 0 && H > 0 && S > 0 && head_dim_ok(D)) {
-    const size_t need = bsattn_fwd_workspace_bytes(B, H, S, D);
-    if (need > 0 && is_causal) {
-      if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0)
-        return BSATTN_ERR_WORKSPACE;
-      const SplitLayout L = split_layout(B, H, nblocks(S), D);
-      unsigned char* ws = (unsigned char*)workspace;
-      a.split_min = kSplitMinBlocks;
-      a.split_row0 = kSplitMinBlocks;   // causal row i holds at most i + 1 blocks
-      a.part_o = (float*)(ws + L.o_off);
-      a.part_ml = (float2*)(ws + L.ml_off);
-      a.part_flag = (int*)(ws + L.flag_off);
-    }
-  }
+  const bsattn_status st = set_long_row_split(a, B, H, S, D, is_causal, workspace, workspace_bytes);
+  if (st != BSATTN_OK) return st;
   return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 
@@ -252,13 +260,16 @@ static bool fused_nb_ok(int D, int S) {
 bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* block_scores, int B, int H, int S, int D, int topk,
                               int dense_last_two_rows, int force_diagonal, int is_causal,
-                              uint8_t* mask_out, uint16_t* out, bsattn_stream_t stream) {
+                              uint8_t* mask_out, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, bsattn_stream_t stream) {
   if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
   if (S > 0 && (topk < 0 || topk > nblocks(S))) return BSATTN_ERR_SHAPE;
   if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
   PrefillArgs a = fwd_args(q, k, v, out, kSrcTopk);
   a.scores = block_scores; a.mask_out = mask_out; a.topk = topk;
   a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;
+  const bsattn_status st = set_long_row_split(a, B, H, S, D, is_causal, workspace, workspace_bytes);
+  if (st != BSATTN_OK) return st;
   return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 
@@ -266,12 +277,15 @@ bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const u
                                    const float* block_scores, int B, int H, int S, int D,
                                    float threshold, int dense_last_two_rows, int force_diagonal,
                                    int is_causal, uint8_t* mask_out, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes,
                                    bsattn_stream_t stream) {
   if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
   if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
   PrefillArgs a = fwd_args(q, k, v, out, kSrcThreshold);
   a.scores = block_scores; a.mask_out = mask_out; a.threshold = threshold;
   a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;
+  const bsattn_status st = set_long_row_split(a, B, H, S, D, is_causal, workspace, workspace_bytes);
+  if (st != BSATTN_OK) return st;
   return fwd_common(a, B, H, S, S, D, is_causal, as_hip(stream));
 }
 

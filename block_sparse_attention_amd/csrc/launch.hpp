@@ -65,7 +65,8 @@ struct PrefillArgs {
   int B, H, Sq, Sk, D, nbq, nbk;   // Sq <= Sk: the queries are the last Sq positions
   int causal;
   int ks;                // D = 64: key splits per work item, 1 or 2 (D = 128 always uses 2)
-  // Long causal rows split in two (kSrcMask, square only; split_min = 0: off).
+  // Long causal rows split in two (mask-row and block-score sources, square
+  // only; split_min = 0: off).
   // Query blocks i >= split_row0 can hold more than split_min key blocks; one
   // extra work-group per such query block takes the second half of its list
   // when it does, both halves leave fp32 partial rows in the workspace, and a

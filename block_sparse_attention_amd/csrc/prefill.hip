@@ -178,10 +178,11 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   int bh, i;
   // Work-groups below n_help take the second half of a long row's list (the
   // query blocks i >= split_row0, heaviest first); the rest are the items.
-  // Only a mask-row source splits (the split logic below is compiled for it
-  // alone), so any other source has no helpers whatever split_min says.
+  // The mask-row and block-score sources split (every work-group of a row
+  // builds the same list); a given list never does, whatever split_min says.
+  constexpr bool kCanSplit = SRC != kSrcList;
   const int n_help =
-      (SRC == kSrcMask && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
+      (kCanSplit && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
   const bool helper = (int)blockIdx.x < n_help;
   if (helper) {
     map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, bh, i);
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // second; a helper whose row is not long has nothing to do.
   int part = -1;   // -1: the whole row, written to out
   int64_t slot = 0;
-  if constexpr (SRC == kSrcMask) {
+  if constexpr (kCanSplit) {
     if (a.split_min > 0 && i >= a.split_row0) {
       slot = (int64_t)bh * (nbq - a.split_row0) + (i - a.split_row0);
       const bool split = nblk > a.split_min;
@@ -765,7 +766,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   }
 
   if constexpr (SRC == kSrcTopk || SRC == kSrcThreshold) {
-    if (w == 0 && a.mask_out) {
+    if (w == 0 && a.mask_out && !helper) {   // the item writes its row, not its helper
       uint8_t* mo = a.mask_out + ((int64_t)bh * nbk + i) * nbk;
 #pragma unroll
       for (int u = 0; u < kMaxKeyChunks; ++u) {
@@ -865,9 +866,9 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     });
     if (e != hipSuccess) return e;
   }
-  // helpers and the merge exist only for the mask-row source
+  // helpers and the merge exist only for the sources that can split
   const int64_t slots =
-      (SRC == kSrcMask && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
+      (SRC != kSrcList && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
   const int64_t items = (int64_t)BH * a.nbq + slots;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
                      group);

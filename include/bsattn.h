@@ -163,26 +163,25 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
  * last two rows; tril; forced diagonal), writes that row to mask_out when
  * mask_out is not NULL (uint8 0/1 [B, H, nb, nb], byte-identical to the
  * builders' output), compacts it, and runs the forward pass of bsattn_fwd on
- * it, every row whole in one work-group (no long-row split, so the output is
- * bit-identical to bsattn_fwd_chunk with Sq = Sk on that mask, and to
- * bsattn_fwd wherever bsattn_fwd does not split).  q/k/v/out and is_causal as
- * bsattn_fwd.
+ * it.  Long causal rows split as in bsattn_fwd (both work-groups of a split
+ * row select the same row; only the first writes it to mask_out), so the
+ * output is bit-identical to bsattn_fwd on that mask and workspace layout.
+ * q/k/v/out, is_causal, workspace and workspace_bytes as bsattn_fwd (the
+ * size is bsattn_fwd_workspace_bytes; NULL when it is 0 or is_causal is 0).
  * Errors: as bsattn_fwd and the builders (topk < 0 or topk > nb: SHAPE);
  * nb > 256 (S > 16384: the row's keys are held in registers) is UNSUPPORTED,
  * where the two-launch path (builder, then bsattn_fwd) applies.
- * Speed: with more than 128 key blocks (S > 8192) and causal masks whose
- * rows can hold more than 128 blocks, the two-launch path is the faster one,
- * since only bsattn_fwd splits long rows; up to 128 blocks the two forms
- * are within a few percent of each other.
  */
 bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* block_scores, int B, int H, int S, int D, int topk,
                               int dense_last_two_rows, int force_diagonal, int is_causal,
-                              uint8_t* mask_out, uint16_t* out, bsattn_stream_t stream);
+                              uint8_t* mask_out, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, bsattn_stream_t stream);
 bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const float* block_scores, int B, int H, int S, int D,
                                    float threshold, int dense_last_two_rows, int force_diagonal,
                                    int is_causal, uint8_t* mask_out, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes,
                                    bsattn_stream_t stream);
 
 /*

@@ -136,15 +136,24 @@ def test_noalloc_decode_validates_on_host():
 def test_fused_fwd_validates_on_host():
     lib = _lib()
     F = FAKE
-    assert lib.bsattn_fwd_topk(None, F, F, F, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None) == 1
-    assert lib.bsattn_fwd_topk(F, F, F, None, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None) == 1
-    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, 5, 0, 1, 1, None, F, None) == 2   # topk > nb
-    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, -1, 0, 1, 1, None, F, None) == 2
-    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 96, 2, 0, 1, 1, None, F, None) == 3
-    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 64 * 257, 64, 2, 0, 1, 1, None, F, None) == 3
-    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 1, 64 * 257, 64, 0.5, 0, 1, 1, None, F, None) == 3
-    assert lib.bsattn_fwd_threshold(F, F, F, None, 1, 1, 256, 64, 0.5, 0, 1, 1, None, F, None) == 1
-    assert lib.bsattn_fwd_threshold(F, F, F, F, 0, 1, 256, 64, 0.5, 0, 1, 1, None, F, None) == 2
+    assert lib.bsattn_fwd_topk(None, F, F, F, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None, 0, None) == 1
+    assert lib.bsattn_fwd_topk(F, F, F, None, 1, 1, 256, 64, 2, 0, 1, 1, None, F, None, 0, None) == 1
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, 5, 0, 1, 1, None, F, None, 0, None) == 2   # topk > nb
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 64, -1, 0, 1, 1, None, F, None, 0, None) == 2
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 256, 96, 2, 0, 1, 1, None, F, None, 0, None) == 3
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 1, 64 * 257, 64, 2, 0, 1, 1, None, F, None, 0, None) == 3
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 1, 64 * 257, 64, 0.5, 0, 1, 1, None, F, None, 0, None) == 3
+    assert lib.bsattn_fwd_threshold(F, F, F, None, 1, 1, 256, 64, 0.5, 0, 1, 1, None, F, None, 0, None) == 1
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 0, 1, 256, 64, 0.5, 0, 1, 1, None, F, None, 0, None) == 2
+    # long causal rows split as in bsattn_fwd, so the same workspace is required
+    S = 8320
+    need = lib.bsattn_fwd_workspace_bytes(1, 8, S, 128)
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 8, S, 128, 2, 0, 1, 1, None, F, None, 0, None) == 4
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 8, S, 128, 0.5, 0, 1, 1, None, F, F, need - 1,
+                                    None) == 4
+    misaligned = ctypes.c_void_p(0x1008)
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 8, S, 128, 2, 0, 1, 1, None, F, misaligned, need,
+                               None) == 4
 
 
 def test_xattn_validates_on_host():

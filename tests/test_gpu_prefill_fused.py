@@ -2,16 +2,17 @@
 
 bsattn_fwd_topk / bsattn_fwd_threshold must write the same mask bytes as the
 stand-alone builders (and as the oracle), and produce outputs bit-identical
-to the mask-driven forward pass on that mask when it runs every row whole
-(the chunk entry with Sq = Sk: the same block lists in the same order).
-bsattn_fwd, which splits causal rows of more than 128 key blocks in two,
-agrees with them within the output tolerance."""
+to bsattn_fwd on that mask: the same block lists in the same order, and the
+same split of causal rows of more than 128 key blocks into two halves and a
+merge.  The chunk entry with Sq = Sk, which runs every row whole, agrees with
+both within the output tolerance (and bit for bit where no row splits)."""
 import numpy as np
 import pytest
 import torch
 
 import block_sparse_attention_amd as bsa
 from block_sparse_attention_amd import inputs as gen
+from oracle import attention as oa
 from oracle import mask as om
 from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
 
@@ -26,9 +27,11 @@ def _both(q, k, v, scores, cfg_kind, param, dense2, diag, causal):
     else:
         m = bsa.bsattn_build_mask_threshold(s, param, dense2, diag)
         fused, fm = bsa.bsattn_fwd_threshold(q, k, v, s, param, dense2, diag, causal, write_mask=True)
-    ref = bsa.bsattn_fwd_chunk(q, k, v, m, causal)
-    split = bsa.bsattn_fwd(q, k, v, m, causal)
-    check_close(gpu_bf16_to_f64(split), gpu_bf16_to_f64(ref), "bsattn_fwd against whole rows")
+    ref = bsa.bsattn_fwd(q, k, v, m, causal)
+    whole = bsa.bsattn_fwd_chunk(q, k, v, m, causal)
+    check_close(gpu_bf16_to_f64(ref), gpu_bf16_to_f64(whole), "bsattn_fwd against whole rows")
+    if q.shape[2] <= 128 * 64 or not causal:   # no row can split
+        assert torch.equal(ref.view(torch.int16), whole.view(torch.int16))
     return m, ref, fm, fused
 
 
@@ -96,3 +99,47 @@ def test_without_mask_output():
     a = bsa.bsattn_fwd_topk(q, k, v, s, cfg.topk)
     b, _ = bsa.bsattn_fwd_topk(q, k, v, s, cfg.topk, write_mask=True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["topk", "threshold"])
+@pytest.mark.parametrize("S,H,D", [(8320, 8, 128), (8300, 4, 64)])
+def test_long_rows_split_like_bsattn_fwd(kind, S, H, D):
+    """Rows of more than 128 selected key blocks split in the fused forms too.
+    Threshold: heavy rows 128 and 129 (129 and 130 blocks, and on odd heads a
+    row 129 of exactly 128 that stays whole), light rows elsewhere, and a last
+    head with no long row (its helpers have nothing to do).  Top-k with
+    k = 129 keeps nearly every causal block, so rows 128 and 129 are long on
+    every head.  The output matches bsattn_fwd bit for bit (one workspace
+    serves both calls) and the oracle on the rows past block 127."""
+    nb = -(-S // 64)
+    rng = np.random.default_rng(S + H + D)
+    scores = rng.random((1, H, nb, nb), dtype=np.float32) * 0.5    # all below 0.9: light rows
+    for h in range(H - 1):
+        scores[0, h, 128, :129] = 1.0
+        scores[0, h, 129, :130] = 1.0
+        if h % 2:
+            scores[0, h, 129, [3, 77]] = 0.0
+    scores[0, :, np.arange(nb), np.arange(nb)] = 1.0
+    qkv = {n: gen.f32_to_bf16_bits(rng.standard_normal((1, H, S, D), dtype=np.float32))
+           for n in ("q", "k", "v")}
+    q, k, v = (to_gpu_bf16(qkv[n]) for n in ("q", "k", "v"))
+    ws = torch.empty(bsa.bsattn_fwd_workspace_bytes(1, H, S, D), dtype=torch.uint8, device="cuda")
+    s = to_gpu(scores)
+    if kind == "topk":
+        param, want_mask = 129, om.build_mask_topk(scores, 129, False, True)
+        fused, fm = bsa.bsattn_fwd_topk(q, k, v, s, param, False, True, True, write_mask=True,
+                                        workspace=ws)
+    else:
+        param, want_mask = 0.9, om.build_mask_threshold(scores, 0.9, False, True)
+        fused, fm = bsa.bsattn_fwd_threshold(q, k, v, s, param, False, True, True, write_mask=True,
+                                             workspace=ws)
+    say(f"[fused] long rows {kind} S={S} H={H} D={D} blocks={int(want_mask.sum())}")
+    np.testing.assert_array_equal(fm.cpu().numpy(), want_mask)
+    assert int(want_mask[0, 0, 129].sum()) == 130
+    ref = bsa.bsattn_fwd(q, k, v, fm, True, workspace=ws)
+    assert torch.equal(fused.view(torch.int16), ref.view(torch.int16))
+    rows = sorted(set(range(127 * 64, S)) | {0, S // 2})
+    x = {n: gen.bf16_bits_to_f64(qkv[n]) for n in qkv}
+    want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], want_mask[0, h],
+                                          True, rows) for h in range(H)])
+    check_close(gpu_bf16_to_f64(fused)[0][:, rows], want, f"fused {kind} long rows S{S} H{H} D{D}")
