@@ -695,16 +695,35 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
                                      o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv};
         }
       if (h == 0) a.part_ml[pr] = float2{m, lt};
-    } else if (qrow < Sq) {
-      uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
+    }
+    if (part < 0) {   // uniform over the work-group
+      // The bf16 output tile is staged in the K slot of the last block (its
+      // K tile was read before the last iteration's barrier; nothing reads
+      // or loads that slot since) in the K tile's swizzled row layout, then
+      // written out as contiguous 16-byte pieces: every wave store covers
+      // whole rows of the query block instead of 8 bytes of 32 rows.
+      unsigned char* const otile = smem + ((max(nblk, 1) - 1) & 1) * C::kTileBytes;
+      const int r = 32 * rg + n;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = 32 * t + 8 * g4 + 4 * h;
-          *(u32x2*)(O + d) = u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
-                                   pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
+          const int g = 4 * t + g4;
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * h) =
+              u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
+                    pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
         }
+      __syncthreads();
+      const int rows = min(64, Sq - q0);
+      uint16_t* __restrict__ Ot = a.out + q_off + (int64_t)q0 * D;
+#pragma unroll
+      for (int it = 0; it < 64 * C::G / C::kThreads; ++it) {
+        const int e = it * C::kThreads + tid;
+        const int rr = e / C::G, g = e % C::G;
+        if (rr < rows)
+          *(u32x4*)(Ot + rr * D + g * 8) =
+              *(const u32x4*)(otile + rr * C::kRowBytes + (g ^ swz_k<D>(rr)) * 16);
+      }
     }
   } else {
   constexpr int kHalf = C::kDT / 2;
@@ -736,9 +755,15 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   const float fa = al_a * inv, fb = al_b * inv;
   // half of a long row: its normalised fp32 output and (row max, row sum)
   const int64_t pr = (slot * 2 + (part < 0 ? 0 : part)) * 64 + 32 * rg + n;
+  // The bf16 output tile is staged in V slot 0 (free since the first barrier
+  // above) in the K tile's swizzled row layout, then written out by the whole
+  // work-group as contiguous 16-byte pieces: the rows of a query block are
+  // contiguous in memory, so every wave store covers whole rows instead of
+  // 8 bytes of 32 different rows.
+  unsigned char* const otile = smem + 2 * C::kTileBytes;
   auto finish = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
-    uint16_t* __restrict__ O = a.out + q_off + (int64_t)qrow * D;
+    const int r = 32 * rg + n;
 #pragma unroll
     for (int t = 0; t < kHalf; ++t) {
       constexpr int kBase = KH * kHalf;
@@ -751,17 +776,31 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
           r4[e] = o[kBase + t][ii] * fa + xin[(t * 16 + ii) * kWave + lane] * fb;
         }
         const int d = 32 * (kBase + t) + 8 * g4 + 4 * h;
-        if (part >= 0)
-          *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
-        else
-          *(u32x2*)(O + d) = u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
+        if (part >= 0) {
+          if (qrow < Sq) *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
+        } else {
+          const int g = d >> 3;
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * h) =
+              u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
+        }
       }
     }
   };
   if (part >= 0 && qrow < Sq && kh == 0 && h == 0) a.part_ml[pr] = float2{M, lt};
-  if (qrow < Sq) {
-    if (kh == 0) finish(std::integral_constant<int, 0>{});
-    else finish(std::integral_constant<int, 1>{});
+  if (kh == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, 1>{});
+  if (part < 0) {   // uniform over the work-group
+    __syncthreads();
+    const int rows = min(64, Sq - q0);
+    uint16_t* __restrict__ Ot = a.out + q_off + (int64_t)q0 * D;
+#pragma unroll
+    for (int it = 0; it < 64 * C::G / C::kThreads; ++it) {
+      const int e = it * C::kThreads + tid;
+      const int r = e / C::G, g = e % C::G;
+      if (r < rows)
+        *(u32x4*)(Ot + r * D + g * 8) =
+            *(const u32x4*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16);
+    }
   }
   }
 
