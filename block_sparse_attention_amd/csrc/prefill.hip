@@ -137,6 +137,16 @@ size_t lds_bytes(int nb) {
   return (size_t)C::kRingBytes + C::kStatsBytes + (size_t)(((nb + 1) * 2 + 15) / 16) * 16;
 }
 
+// The staged output tile: row r's 16-byte granule g sits at granule
+// g ^ swz_k(r) of the row, with its two 8-byte halves swapped in rows with
+// bit 4 set, so the per-lane 8-byte writes of 32 rows (two lanes per
+// granule) and the 16-byte reads of whole rows both avoid bank conflicts.
+template <int D>
+__device__ __forceinline__ u32x4 staged_row_piece(const unsigned char* tile, int r, int g) {
+  const u32x4 v = *(const u32x4*)(tile + r * (D * 2) + (g ^ swz_k<D>(r)) * 16);
+  return (r >> 4) & 1 ? u32x4{v[2], v[3], v[0], v[1]} : v;
+}
+
 // S^T of one block for one wave: NT tiles of 32 keys x its 32 query rows.
 template <int NT>
 struct Scores {
@@ -709,7 +719,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int g = 4 * t + g4;
-          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * h) =
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ ((r >> 4) & 1))) =
               u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
                     pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
         }
@@ -721,8 +731,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         const int e = it * C::kThreads + tid;
         const int rr = e / C::G, g = e % C::G;
         if (rr < rows)
-          *(u32x4*)(Ot + rr * D + g * 8) =
-              *(const u32x4*)(otile + rr * C::kRowBytes + (g ^ swz_k<D>(rr)) * 16);
+          *(u32x4*)(Ot + rr * D + g * 8) = staged_row_piece<D>(otile, rr, g);
       }
     }
   } else {
@@ -780,7 +789,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
           if (qrow < Sq) *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
         } else {
           const int g = d >> 3;
-          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * h) =
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ ((r >> 4) & 1))) =
               u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
         }
       }
@@ -797,9 +806,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     for (int it = 0; it < 64 * C::G / C::kThreads; ++it) {
       const int e = it * C::kThreads + tid;
       const int r = e / C::G, g = e % C::G;
-      if (r < rows)
-        *(u32x4*)(Ot + r * D + g * 8) =
-            *(const u32x4*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16);
+      if (r < rows) *(u32x4*)(Ot + r * D + g * 8) = staged_row_piece<D>(otile, r, g);
     }
   }
   }
