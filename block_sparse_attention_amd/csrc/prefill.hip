@@ -138,13 +138,18 @@ size_t lds_bytes(int nb) {
 }
 
 // The staged output tile: row r's 16-byte granule g sits at granule
-// g ^ swz_k(r) of the row, with its two 8-byte halves swapped in rows with
-// bit 4 set, so the per-lane 8-byte writes of 32 rows (two lanes per
-// granule) and the 16-byte reads of whole rows both avoid bank conflicts.
+// g ^ swz_k(r) of the row, with its two 8-byte halves swapped in the rows
+// staged_swap marks, so both the per-lane 8-byte writes (one granule half
+// per lane, 32 rows per instruction) and the 16-byte reads of whole rows
+// are free of bank conflicts (checked against a 32- and a 64-bank model).
+template <int D>
+__device__ __forceinline__ int staged_swap(int r) {
+  return D == 128 ? ((r >> 3) ^ (r >> 4)) & 1 : (r ^ (r >> 4)) & 1;
+}
 template <int D>
 __device__ __forceinline__ u32x4 staged_row_piece(const unsigned char* tile, int r, int g) {
   const u32x4 v = *(const u32x4*)(tile + r * (D * 2) + (g ^ swz_k<D>(r)) * 16);
-  return (r >> 4) & 1 ? u32x4{v[2], v[3], v[0], v[1]} : v;
+  return staged_swap<D>(r) ? u32x4{v[2], v[3], v[0], v[1]} : v;
 }
 
 // S^T of one block for one wave: NT tiles of 32 keys x its 32 query rows.
@@ -719,7 +724,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int g = 4 * t + g4;
-          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ ((r >> 4) & 1))) =
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ staged_swap<D>(r))) =
               u32x2{pack_bf16x2(o[t][4 * g4 + 0] * inv, o[t][4 * g4 + 1] * inv),
                     pack_bf16x2(o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv)};
         }
@@ -789,7 +794,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
           if (qrow < Sq) *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
         } else {
           const int g = d >> 3;
-          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ ((r >> 4) & 1))) =
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ staged_swap<D>(r))) =
               u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
         }
       }
