@@ -716,7 +716,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       // K tile was read before the last iteration's barrier; nothing reads
       // or loads that slot since) in the K tile's swizzled row layout, then
       // written out as contiguous 16-byte pieces: every wave store covers
-      // whole rows of the query block instead of 8 bytes of 32 rows.
+      // whole rows of the query block instead of 8 bytes of 32 rows.  The
+      // output is not read again here, so the stores are non-temporal.
       unsigned char* const otile = smem + ((max(nblk, 1) - 1) & 1) * C::kTileBytes;
       const int r = 32 * rg + n;
 #pragma unroll
@@ -736,7 +737,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
         const int e = it * C::kThreads + tid;
         const int rr = e / C::G, g = e % C::G;
         if (rr < rows)
-          *(u32x4*)(Ot + rr * D + g * 8) = staged_row_piece<D>(otile, rr, g);
+          __builtin_nontemporal_store(staged_row_piece<D>(otile, rr, g),
+                                      (u32x4*)(Ot + rr * D + g * 8));
       }
     }
   } else {
@@ -773,7 +775,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // above) in the K tile's swizzled row layout, then written out by the whole
   // work-group as contiguous 16-byte pieces: the rows of a query block are
   // contiguous in memory, so every wave store covers whole rows instead of
-  // 8 bytes of 32 different rows.
+  // 8 bytes of 32 different rows (non-temporal: nothing here reads it again).
   unsigned char* const otile = smem + 2 * C::kTileBytes;
   auto finish = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
@@ -811,7 +813,8 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
     for (int it = 0; it < 64 * C::G / C::kThreads; ++it) {
       const int e = it * C::kThreads + tid;
       const int r = e / C::G, g = e % C::G;
-      if (r < rows) *(u32x4*)(Ot + r * D + g * 8) = staged_row_piece<D>(otile, r, g);
+      if (r < rows)
+        __builtin_nontemporal_store(staged_row_piece<D>(otile, r, g), (u32x4*)(Ot + r * D + g * 8));
     }
   }
   }
