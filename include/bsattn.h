@@ -132,7 +132,8 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
  * Errors: NULL pointers; B, H, S <= 0 (SHAPE); D not 64 or 128 (UNSUPPORTED);
  * workspace NULL, misaligned or below bsattn_fwd_workspace_bytes (WORKSPACE).
  */
-/* Workspace of bsattn_fwd: nonzero when S spans more than 128 key blocks
+/* Workspace of bsattn_fwd (and of the fused bsattn_fwd_topk and
+ * bsattn_fwd_threshold): nonzero when S spans more than 128 key blocks
  * (B * H * (nb - 128) query blocks can split, each needing two fp32
  * [64, D] halves, 2 x 64 (row max, row sum) pairs and a flag, every part
  * 256-byte aligned); 0 when no row can split, when the split would need more
