@@ -277,6 +277,9 @@ def bsattn_fwd_indices(q, k, v, idx, cnt, is_causal: bool = True, out=None, stre
     return out
 
 
+FUSED_MAX_BLOCKS = 256   # the one-launch fused forms hold a row of up to 256 key blocks
+
+
 def _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream):
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
@@ -288,7 +291,9 @@ def _fused_setup(q, k, v, scores, out, mask_out, write_mask, stream):
         out = _empty(q.shape, q.dtype, q.device, stream)
     _dev(out, "out", torch.bfloat16, 4)
     mask = mask_out
-    if mask is None and write_mask:
+    if mask is None and (write_mask or nb > FUSED_MAX_BLOCKS):
+        # past FUSED_MAX_BLOCKS key blocks the call runs as builder + forward
+        # and needs a mask buffer between the two
         mask = _empty((B, H, nb, nb), torch.uint8, q.device, stream)
     if mask is not None:
         _dev(mask, "mask_out", torch.uint8, 4)

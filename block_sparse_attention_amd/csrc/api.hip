@@ -172,10 +172,8 @@ size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
   return split_layout(B, H, nblocks(S), D).bytes;
 }
 
-// Shared checks and launch of the forward forms; `a` carries the
-// source-specific pointers (mask, list, or block scores).
-static bsattn_status fwd_common(PrefillArgs a, int B, int H, int Sq, int Sk, int D, int is_causal,
-                                hipStream_t stream) {
+// The shape checks every forward form shares.
+static bsattn_status fwd_check(int B, int H, int Sq, int Sk, int D) {
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
   if ((long long)B * H * nblocks(Sq) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
@@ -183,6 +181,15 @@ static bsattn_status fwd_common(PrefillArgs a, int B, int H, int Sq, int Sk, int
   if (nblocks(Sk) > 65535 || prefill_lds_bytes(D, nblocks(Sk)) > kMaxLdsBytes)
     return BSATTN_ERR_UNSUPPORTED;
   if (!fits_elems((long double)B * H * Sk * D)) return BSATTN_ERR_SHAPE;
+  return BSATTN_OK;
+}
+
+// Shared checks and launch of the forward forms; `a` carries the
+// source-specific pointers (mask, list, or block scores).
+static bsattn_status fwd_common(PrefillArgs a, int B, int H, int Sq, int Sk, int D, int is_causal,
+                                hipStream_t stream) {
+  const bsattn_status st = fwd_check(B, H, Sq, Sk, D);
+  if (st != BSATTN_OK) return st;
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
   a.nbq = nblocks(Sq); a.nbk = nblocks(Sk);
   a.causal = is_causal ? 1 : 0;
@@ -257,6 +264,25 @@ static bool fused_nb_ok(int D, int S) {
   return nblocks(S) <= 256;
 }
 
+// Rows too long for the one-launch form: the builder writes the mask to
+// mask_out, then the mask-row forward runs on it (the same mask bytes and
+// the same output as one launch would give).  Every check runs before the
+// first launch.
+extern "C++" template <class Build>
+static bsattn_status fused_two_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      int B, int H, int S, int D, int is_causal, uint8_t* mask_out,
+                                      uint16_t* out, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream, Build build) {
+  if (!mask_out) return BSATTN_ERR_UNSUPPORTED;
+  PrefillArgs a = fwd_args(q, k, v, out, kSrcMask);
+  a.mask = mask_out;
+  bsattn_status st = set_long_row_split(a, B, H, S, D, is_causal, workspace, workspace_bytes);
+  if (st == BSATTN_OK) st = fwd_check(B, H, S, S, D);
+  if (st != BSATTN_OK) return st;
+  if (build() != hipSuccess) return BSATTN_ERR_HIP;
+  return fwd_common(a, B, H, S, S, D, is_causal, stream);
+}
+
 bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* block_scores, int B, int H, int S, int D, int topk,
                               int dense_last_two_rows, int force_diagonal, int is_causal,
@@ -264,7 +290,14 @@ bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16
                               size_t workspace_bytes, bsattn_stream_t stream) {
   if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
   if (S > 0 && (topk < 0 || topk > nblocks(S))) return BSATTN_ERR_SHAPE;
-  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
+  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S))
+    return fused_two_launch(q, k, v, B, H, S, D, is_causal, mask_out, out, workspace,
+                            workspace_bytes, as_hip(stream), [&]() {
+                              return launch_mask_topk(block_scores, B, H, nblocks(S), topk,
+                                                      dense_last_two_rows ? 1 : 0,
+                                                      force_diagonal ? 1 : 0, mask_out,
+                                                      as_hip(stream));
+                            });
   PrefillArgs a = fwd_args(q, k, v, out, kSrcTopk);
   a.scores = block_scores; a.mask_out = mask_out; a.topk = topk;
   a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;
@@ -280,7 +313,14 @@ bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const u
                                    void* workspace, size_t workspace_bytes,
                                    bsattn_stream_t stream) {
   if (!q || !k || !v || !block_scores || !out) return BSATTN_ERR_NULL;
-  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S)) return BSATTN_ERR_UNSUPPORTED;
+  if (S > 0 && head_dim_ok(D) && !fused_nb_ok(D, S))
+    return fused_two_launch(q, k, v, B, H, S, D, is_causal, mask_out, out, workspace,
+                            workspace_bytes, as_hip(stream), [&]() {
+                              return launch_mask_threshold(block_scores, B, H, nblocks(S),
+                                                           threshold, dense_last_two_rows ? 1 : 0,
+                                                           force_diagonal ? 1 : 0, mask_out,
+                                                           as_hip(stream));
+                            });
   PrefillArgs a = fwd_args(q, k, v, out, kSrcThreshold);
   a.scores = block_scores; a.mask_out = mask_out; a.threshold = threshold;
   a.dense2 = dense_last_two_rows ? 1 : 0; a.diag = force_diagonal ? 1 : 0;

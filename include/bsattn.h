@@ -169,9 +169,12 @@ bsattn_status bsattn_fwd_indices(const uint16_t* q, const uint16_t* k, const uin
  * output is bit-identical to bsattn_fwd on that mask and workspace layout.
  * q/k/v/out, is_causal, workspace and workspace_bytes as bsattn_fwd (the
  * size is bsattn_fwd_workspace_bytes; NULL when it is 0 or is_causal is 0).
+ * With nb > 256 (S > 16384) a row's keys no longer fit the registers the
+ * one-launch form holds them in: the call then runs as two launches, the
+ * builder writing mask_out and bsattn_fwd reading it, with the same mask
+ * bytes and output; mask_out is required there (NULL: UNSUPPORTED).
  * Errors: as bsattn_fwd and the builders (topk < 0 or topk > nb: SHAPE);
- * nb > 256 (S > 16384: the row's keys are held in registers) is UNSUPPORTED,
- * where the two-launch path (builder, then bsattn_fwd) applies.
+ * all are reported before anything is launched.
  */
 bsattn_status bsattn_fwd_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* block_scores, int B, int H, int S, int D, int topk,

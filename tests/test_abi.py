@@ -154,6 +154,18 @@ def test_fused_fwd_validates_on_host():
     misaligned = ctypes.c_void_p(0x1008)
     assert lib.bsattn_fwd_topk(F, F, F, F, 1, 8, S, 128, 2, 0, 1, 1, None, F, misaligned, need,
                                None) == 4
+    # past 256 key blocks the fused forms run as builder + forward through mask_out; every
+    # check (mask_out present, workspace, shapes) still comes before the first launch
+    S2 = 64 * 260
+    need2 = lib.bsattn_fwd_workspace_bytes(1, 2, S2, 64)
+    assert need2 > 0
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 2, S2, 64, 2, 0, 1, 1, None, F, F, need2, None) == 3
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 2, S2, 64, 2, 0, 1, 1, F, F, None, 0, None) == 4
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 2, S2, 64, 0.5, 0, 1, 1, F, F, F, need2 - 1,
+                                    None) == 4
+    assert lib.bsattn_fwd_threshold(F, F, F, F, 1, 2, S2, 96, 0.5, 0, 1, 1, F, F, None, 0,
+                                    None) == 3
+    assert lib.bsattn_fwd_topk(F, F, F, F, 1, 2, S2, 64, 261, 0, 1, 1, F, F, F, need2, None) == 2
 
 
 def test_xattn_validates_on_host():

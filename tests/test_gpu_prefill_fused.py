@@ -143,3 +143,37 @@ def test_long_rows_split_like_bsattn_fwd(kind, S, H, D):
     want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], want_mask[0, h],
                                           True, rows) for h in range(H)])
     check_close(gpu_bf16_to_f64(fused)[0][:, rows], want, f"fused {kind} long rows S{S} H{H} D{D}")
+
+
+@pytest.mark.parametrize("kind", ["topk", "threshold"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_past_256_blocks_runs_as_two_launches(kind, causal):
+    """Past 256 key blocks a row no longer fits the one-launch prologue: the
+    call builds the mask into mask_out and runs the mask-row forward on it,
+    with the builder's mask bytes and bsattn_fwd's output."""
+    B, H, S, D = 1, 2, 64 * 260 - 20, 64
+    nb = -(-S // 64)
+    rng = np.random.default_rng(260 + causal)
+    scores = rng.random((B, H, nb, nb), dtype=np.float32)
+    qkv = {n: gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D), dtype=np.float32))
+           for n in ("q", "k", "v")}
+    q, k, v = (to_gpu_bf16(qkv[n]) for n in ("q", "k", "v"))
+    s = to_gpu(scores)
+    say(f"[fused] {kind} past 256 blocks: nb={nb} causal={causal}")
+    if kind == "topk":
+        fused, fm = bsa.bsattn_fwd_topk(q, k, v, s, 12, True, True, causal, write_mask=True)
+        bare = bsa.bsattn_fwd_topk(q, k, v, s, 12, True, True, causal)
+        want_mask = om.build_mask_topk(scores, 12, True, True)
+    else:
+        fused, fm = bsa.bsattn_fwd_threshold(q, k, v, s, 0.95, True, True, causal, write_mask=True)
+        bare = bsa.bsattn_fwd_threshold(q, k, v, s, 0.95, True, True, causal)
+        want_mask = om.build_mask_threshold(scores, 0.95, True, True)
+    np.testing.assert_array_equal(fm.cpu().numpy(), want_mask)
+    ref = bsa.bsattn_fwd(q, k, v, fm, causal)
+    assert torch.equal(fused.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(bare.view(torch.int16), ref.view(torch.int16))
+    rows = [0, 63, 64 * 128 + 5, 64 * 200, S - 65, S - 1]
+    x = {n: gen.bf16_bits_to_f64(qkv[n]) for n in qkv}
+    want = np.stack([oa.prefill_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], want_mask[0, h],
+                                          causal, rows) for h in range(H)])
+    check_close(gpu_bf16_to_f64(fused)[0][:, rows], want, f"fused {kind} nb={nb} causal={causal}")
