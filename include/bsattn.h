@@ -6,7 +6,8 @@
  * The library never allocates device memory (its one static array, the
  * scratch of bsattn_decode_gqa_noalloc, is part of the loaded code object)
  * and never synchronises the host: each call only enqueues kernels on `stream` (a hipStream_t; NULL =
- * the default stream).  Outputs are valid once the stream reaches the end of
+ * the default stream) — kernel launches only, no memset or copy, so calls can
+ * be captured into a HIP graph and replayed.  Outputs are valid once the stream reaches the end of
  * the call.  Equal inputs give bitwise equal outputs (no atomics on any
  * value path).
  *
