@@ -1,6 +1,7 @@
 // C ABI of the block-sparse attention library: argument checks and launches.
 // All checks run before anything is enqueued; see include/bsattn.h.
 #include <atomic>
+#include <cstring>
 #include <math.h>
 
 #include "../../include/bsattn.h"
@@ -14,13 +15,20 @@ inline hipStream_t as_hip(bsattn_stream_t s) { return reinterpret_cast<hipStream
 
 inline bool head_dim_ok(int D) { return D == 64 || D == 128; }
 
-inline int nblocks(int n) { return (n + BSATTN_BLOCK - 1) / BSATTN_BLOCK; }
+// 64-token blocks covering n tokens (0 for n <= 0; no overflow near INT_MAX)
+inline int nblocks(int n) {
+  return n <= 0 ? 0 : (int)(((long long)n + BSATTN_BLOCK - 1) / BSATTN_BLOCK);
+}
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // int32 sizes whose products index 64-bit element offsets
 inline bool fits_elems(long double n) { return n < 9.0e18L; }
+// a * b * c of sizes that are each an int, without integer overflow (the
+// product of three ints can pass 2^63; only its comparison with a bound is
+// used, which the 64-bit mantissa keeps exact at these bounds).
+inline long double prod3(long long a, long long b, long long c) { return (long double)a * b * c; }
 
 // Split count of the guide's heuristic (TileLang block-sparse Flash-Attention
 // guide, §6.3), written for decode: one (batch, KV head) pair is one m-block.
@@ -119,7 +127,11 @@ void* decode_scratch_ptr() {
 extern "C" {
 
 const char* bsattn_status_string(bsattn_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the code's bits, not the enum value
+  // (an out-of-range value of the enum type is undefined in C++).
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case BSATTN_OK: return "ok";
     case BSATTN_ERR_NULL: return "null pointer argument";
     case BSATTN_ERR_SHAPE: return "size out of range or inconsistent";
@@ -137,7 +149,7 @@ bsattn_status bsattn_build_mask_topk(const float* scores, int B, int H, int nb, 
                                      bsattn_stream_t stream) {
   if (!scores || !mask) return BSATTN_ERR_NULL;
   if (B <= 0 || H <= 0 || nb <= 0 || topk < 0 || topk > nb) return BSATTN_ERR_SHAPE;
-  if ((long long)B * H * nb > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (prod3(B, H, nb) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   return launch_mask_topk(scores, B, H, nb, topk, dense_last_two_rows ? 1 : 0,
                           force_diagonal ? 1 : 0, mask, as_hip(stream)) == hipSuccess
              ? BSATTN_OK
@@ -160,7 +172,7 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
                                      int32_t* idx, int32_t* cnt, bsattn_stream_t stream) {
   if (!mask || !idx || !cnt) return BSATTN_ERR_NULL;
   if (B <= 0 || H <= 0 || nb <= 0) return BSATTN_ERR_SHAPE;
-  if ((long long)B * H * nb / 4 + 1 > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (prod3(B, H, nb) / 4 + 1 > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   return launch_compact(mask, B, H, nb, is_causal ? 1 : 0, idx, cnt, as_hip(stream)) == hipSuccess
              ? BSATTN_OK
              : BSATTN_ERR_HIP;
@@ -168,7 +180,7 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
 
 size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
   if (B <= 0 || H <= 0 || S <= 0 || !head_dim_ok(D)) return 0;
-  if ((long long)B * H * nblocks(S) > 0x7fffffffLL) return 0;
+  if (prod3(B, H, nblocks(S)) > 0x7fffffffLL) return 0;
   return split_layout(B, H, nblocks(S), D).bytes;
 }
 
@@ -176,7 +188,7 @@ size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
 static bsattn_status fwd_check(int B, int H, int Sq, int Sk, int D) {
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
-  if ((long long)B * H * nblocks(Sq) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (prod3(B, H, nblocks(Sq)) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   // block lists are held as 16-bit entries in LDS next to the K/V ring
   if (nblocks(Sk) > 65535 || prefill_lds_bytes(D, nblocks(Sk)) > kMaxLdsBytes)
     return BSATTN_ERR_UNSUPPORTED;
@@ -515,7 +527,7 @@ bsattn_status xattn_sums_common(const uint16_t* q, const uint16_t* k, int B, int
 
 bsattn_status cumulative_check(int B, int H, int nbq, int nbk) {
   if (B <= 0 || H <= 0 || nbq <= 0 || nbk < nbq) return BSATTN_ERR_SHAPE;
-  if ((long long)B * H * nbq > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
+  if (prod3(B, H, nbq) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   if (nbk > xattn_max_key_blocks()) return BSATTN_ERR_UNSUPPORTED;
   return BSATTN_OK;
 }
