@@ -83,7 +83,11 @@ int device_cu_count() {
   return cus;
 }
 
-size_t decode_ws(int B, int Hq, int D, int ns) {
+// A decode call's partial outputs (one per batch, query head and split):
+// at most 2^31 - 1, so the sizes below cannot wrap.
+inline bool decode_parts_ok(int B, int Hq, int ns) { return prod3(B, Hq, ns) <= 2147483647.0L; }
+
+size_t decode_ws(int B, int Hq, int D, int ns) {   // callers check decode_parts_ok first
   if (ns <= 1) return 0;
   const size_t parts = (size_t)B * Hq * ns;
   return align_up(parts * D * sizeof(float)) + align_up(parts * sizeof(float));
@@ -359,6 +363,7 @@ int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks
 
 size_t bsattn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  if (D > 65536 || !decode_parts_ok(B, Hq, num_splits)) return 0;
   return decode_ws(B, Hq, D, num_splits);
 }
 
@@ -385,6 +390,7 @@ bsattn_status decode_common(DecodeArgs a, int slots, int num_splits, void* works
     ns = bsattn_decode_default_splits(a.B, a.Hq, a.Hkv, slots, a.D);
     if (ns <= 0) return BSATTN_ERR_HIP;
   }
+  if (!decode_parts_ok(a.B, a.Hq, ns)) return BSATTN_ERR_SHAPE;
   const size_t need = decode_ws(a.B, a.Hq, a.Dv, ns);
   if (static_scratch && need > 0) {
     // the no-allocation form: the partials go to the static scratch array
@@ -538,6 +544,7 @@ extern "C" {
 
 size_t bsattn_xattn_workspace_bytes(int B, int H, int Sq, int Sk, int stride) {
   if (!xattn_shape_ok(B, H, Sq, Sk, stride)) return 0;
+  if (nblocks(Sk) > xattn_max_key_blocks()) return 0;   // unsupported: no size can serve it
   return align_up(xattn_lse_bytes(B, H, Sq, Sk, stride)) +
          align_up(xattn_sums_bytes(B, H, Sq, Sk));
 }

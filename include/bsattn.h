@@ -230,7 +230,8 @@ int bsattn_decode_num_splits(int B, int Hq, int Hkv, int max_selected_blocks, in
  * and one log-sum-exp per split) — fp32 partial outputs [B, Hq, splits, Dv]
  * and their base-2 log-sum-exp [B, Hq, splits], each part 256-byte aligned;
  * Dv is the value head dim.  0 when num_splits is 1 (the split kernel then
- * writes out directly) or an argument is out of range. */
+ * writes out directly) or an argument is out of range (including more than
+ * 2^31 - 1 partials, B * Hq * num_splits, which the decode refuses). */
 size_t bsattn_decode_workspace_bytes(int B, int Hq, int Dv, int num_splits);
 
 /*
@@ -258,7 +259,8 @@ size_t bsattn_decode_workspace_bytes(int B, int Hq, int Dv, int num_splits);
  * A sequence whose cu_seqlens_k range is decreasing or ends beyond total_k
  * is treated as empty.
  * Errors: NULL pointers; B, Hq, Hkv, max_selected_blocks, total_k <= 0,
- * Hq % Hkv != 0, num_splits > max_selected_blocks (SHAPE); D or Dv not 64 or
+ * Hq % Hkv != 0, num_splits > max_selected_blocks, B * Hq * num_splits
+ * above 2^31 - 1 (SHAPE); D or Dv not 64 or
  * 128, or Hq / Hkv > 64 (UNSUPPORTED); workspace smaller than
  * bsattn_decode_workspace_bytes for the split count used (WORKSPACE).
  */
@@ -375,6 +377,7 @@ int bsattn_decode_default_splits(int B, int Hq, int Hkv, int max_selected_blocks
  * D not 64 or 128, stride not 4, 8 or 16, nbk > 1024 (UNSUPPORTED);
  * workspace missing or smaller than bsattn_xattn_workspace_bytes (WORKSPACE).
  */
+/* 0 for sizes the estimator refuses (shape or key-block count). */
 size_t bsattn_xattn_workspace_bytes(int B, int H, int Sq, int Sk, int stride);
 
 bsattn_status bsattn_xattn_block_sums(const uint16_t* q, const uint16_t* k, int B, int H, int Sq,

@@ -100,6 +100,14 @@ int main(void) {
   CHECK(bsattn_decode_gqa_paged(h, h, h, ci, ci, NULL, 8, 32, 8, 128, 128, 100, 256, 16, 64, 4, ho,
                                 ws, 1 << 30, NULL), BSATTN_ERR_NULL);
 
+  /* sizes whose products would wrap are refused, never wrapped into a small workspace */
+  CHECK(bsattn_decode_workspace_bytes(65535, 1 << 22, 128, big) == 0, 1);
+  CHECK(bsattn_decode_gqa(h, h, h, ci, ci, 65535, 64, 1, 128, 128, big, 100, big, ho, ws, 1 << 20,
+                          NULL), BSATTN_ERR_SHAPE);
+  CHECK(bsattn_decode_gqa_noalloc(h, h, h, ci, ci, 65535, 64, 1, 128, 128, big, 100, big, ho, NULL),
+        BSATTN_ERR_SHAPE);
+  CHECK(bsattn_xattn_workspace_bytes(1, 1, 64, 64 * 100000, 8) == 0, 1);
+
   /* estimator */
   CHECK(bsattn_xattn_block_sums(NULL, h, 1, 1, 256, 256, 64, 8, 1.0f, 1, fo, ws, 1 << 30, NULL),
         BSATTN_ERR_NULL);
