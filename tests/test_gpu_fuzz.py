@@ -26,9 +26,11 @@ def check_guide(got, want, what):
     atol = rtol = 1e-2, elementwise |got - want| <= 1e-2 + 1e-2 |want|), plus
     the mean absolute error bound.  Used only past the workloads' logit
     scales (q and k at 3x N(0,1), D = 128: logits with a standard deviation
-    near 9), where a sharply peaked softmax whose probabilities are rounded to
-    bfloat16 for the P.V product (as in the guide's kernel) moves a large
-    output by more than the stated 1e-2 absolute."""
+    near 9), where a sharply peaked softmax makes outputs copies of single V
+    values, some of magnitude 4 or more; bfloat16 numbers there are 1/32
+    apart, so storing the output alone can be off by up to 1/64 > 1e-2 (the
+    worst case measured: 4.2654 stored as 4.25, with the value before the
+    store within 4e-5 of the oracle)."""
     assert got.shape == want.shape and np.isfinite(got).all(), what
     err = np.abs(got - want)
     bound = 1e-2 + 1e-2 * np.abs(want)
