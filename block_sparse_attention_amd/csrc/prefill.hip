@@ -576,16 +576,27 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
 #define BSATTN_AHEAD 2
 #endif
   constexpr int kAhead = BSATTN_AHEAD;       // LDS operand reads issued this many slots ahead
+  // At D = 128 the iteration's two tile loads go out in two bursts: V right
+  // after the barrier, K after the last P.V slot (K_{t+2} is first read one
+  // iteration later).  A work-group's 32 KiB in one burst measured 3-4%
+  // slower at B4 H32 S8192; at D = 64 the split made no difference.
+  constexpr int kKIssueSlot = D == 128 ? kPvMfma - 1 : -1;
   auto steady = [&](auto kt, auto kn, auto vt, auto vp, int t, Sc& s_cur, Sc& s_next,
                     const Pr& p_prev, Pr& p_cur) {
     constexpr uint32_t kN = decltype(kn)::value;
     constexpr uint32_t kVP = decltype(vp)::value;
+    // Both list entries are read before the wait and the barrier, so their
+    // LDS round trips overlap the wait.
     const int jt = __builtin_amdgcn_readfirstlane((int)list[t]);
+    const int jn = __builtin_amdgcn_readfirstlane((int)list[t + 2 < nblk ? t + 2 : t + 1]);
     wait_vmem<0>();
     barrier_raw();
     issue(vt, IsV{}, jt);
-    if (t + 2 < nblk) issue(kt, IsK{}, list[t + 2]);
-    else issue(kt, IsV{}, list[t + 1]);   // the last block's V, into the K slot nothing needs
+    auto issue_k = [&]() {
+      if (t + 2 < nblk) issue(kt, IsK{}, jn);
+      else issue(kt, IsV{}, jn);   // the last block's V, into the K slot nothing needs
+    };
+    if constexpr (kKIssueSlot < 0) issue_k();
     if (needs_mask(jt)) mask_block(jt, s_cur);
 
     u32x4 op[kSlots];
@@ -633,6 +644,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       if constexpr (k + kAhead < kSlots) read(std::integral_constant<int, k + kAhead>{});
       mfma(k_c);
       valu(k_c);
+      if constexpr (k == kKIssueSlot) issue_k();
       __builtin_amdgcn_sched_barrier(0);
     });
     // keep the first pass ahead of the redo test
