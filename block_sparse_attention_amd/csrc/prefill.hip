@@ -42,7 +42,7 @@
 //   immediate.
 // * Work items are issued heaviest-first (last query block first), and when
 //   batch*heads is a multiple of 8 each head's items stay on one XCD so its
-//   K/V stay in that XCD's L2.
+//   K/V stay in that XCD's L2 (item_order.hpp).
 // * Long causal rows (more than split_min key blocks, when the caller gives a
 //   workspace) run as two halves in two work-groups; each leaves fp32 rows
 //   plus (row max, row sum), and a small merge launch combines them by the
@@ -55,6 +55,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "item_order.hpp"
 #include "launch.hpp"
 
 namespace bsattn {
@@ -95,30 +96,6 @@ __device__ __forceinline__ int swz_k(int r) {
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? ((r & 2) << 1) : ((r & 3) << 2);
-}
-
-
-// Work item L -> (batch*head, query block).  Query blocks are issued last
-// first.  In mode 1 (batch*heads divisible by 8) item L runs on XCD L % 8;
-// the XCD owns heads xcd, xcd+8, ...; it walks them in groups of `group`
-// heads, query blocks descending, heads interleaved within a group.
-__device__ __forceinline__ void map_item(int L, int BH, int nb, int mode, int group, int& bh,
-                                         int& i) {
-  if (mode == 1) {
-    const int xcd = L & 7;
-    const int k = L >> 3;
-    const int per = group * nb;
-    const int grp = k / per;
-    const int r = k - grp * per;
-    const int ii = r / group;
-    const int hh = grp * group + (r - ii * group);
-    i = nb - 1 - ii;
-    bh = xcd + 8 * hh;
-  } else {
-    const int ii = L / BH;
-    bh = L - ii * BH;
-    i = nb - 1 - ii;
-  }
 }
 
 
@@ -168,7 +145,7 @@ constexpr int kMaxKeyChunks = 4;   // fused row selection handles up to 256 key 
 
 template <int D, int KS, bool CAUSAL, int SRC>
 __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, int map_mode,
-                                                                  int group) {
+                                                                  int group, int lead, int ahead) {
   using C = Cfg<D, KS>;
   constexpr int kWaves = C::kWaves;
   constexpr int NT = C::NT;
@@ -200,10 +177,10 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       (kCanSplit && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
   const bool helper = (int)blockIdx.x < n_help;
   if (helper) {
-    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, bh, i);
+    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, 0, 0, bh, i);
     i += a.split_row0;
   } else {
-    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, bh, i);
+    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, lead, ahead, bh, i);
   }
 
   const int64_t q_off = (int64_t)bh * Sq * D;
@@ -913,15 +890,27 @@ __global__ __launch_bounds__(256) void prefill_split_merge_kernel(PrefillArgs a,
 template <int D, int KS, bool CAUSAL, int SRC>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
-  int mode = 0, group = 1;
+  // Item order (item_order.hpp).  Heads per group: as many as one XCD's
+  // 4 MB L2 holds the K/V of, but at least two: with one head per group a
+  // dense last row (~110 us at B4 H32 S8192 D128) outlasts its head's turn
+  // and the last head's rows trail the launch (two per group measured 2%
+  // faster there, 3.5% at B1 H32 S16384 D128).  At D = 64 the two heaviest
+  // rows of each group are also issued two groups early (6% faster at B4
+  // H32 S8192 D64); at D = 128 that measured no faster, since those rows
+  // then find their K/V outside the L2 the current group fills.
+  int mode = 0, group = 1, lead = 0, ahead = 0;
   if (BH % 8 == 0) {
     mode = 1;
     const int per_xcd = BH / 8;
     const double kv_bytes = 2.0 * a.Sk * D * 2.0;
-    int g = (int)(4.0 * 1024 * 1024 / kv_bytes);
+    int g = max(2, (int)(4.0 * 1024 * 1024 / kv_bytes));
     g = max(1, min(g, per_xcd));
     while (per_xcd % g) --g;
     group = g;
+    if (D == 64) {
+      lead = 2;
+      ahead = 2;
+    }
   }
   const size_t lds = lds_bytes<D, KS>(a.nbk);
   auto kern = prefill_kernel<D, KS, CAUSAL, SRC>;
@@ -937,7 +926,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
       (SRC != kSrcList && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
   const int64_t items = (int64_t)BH * a.nbq + slots;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
-                     group);
+                     group, lead, ahead);
   if (slots > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

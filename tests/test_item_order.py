@@ -1,0 +1,123 @@
+"""The forward's work-item order (csrc/item_order.hpp), compiled for the host.
+
+map_item must be a bijection from work-group index to (batch*head, query
+block); in mode 1 each item must run on the XCD that owns its head
+(bh % 8 == L % 8); and the order must be the one the header describes, which
+this test builds independently by concatenating lists: per XCD, the heavy
+items (the first `lead` query blocks, descending) of groups 0 .. ahead-1,
+then for each group j the heavy items of group j + ahead followed by group
+j's remaining query blocks, heads interleaved within a group."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HDR = os.path.join(HERE, "..", "block_sparse_attention_amd", "csrc")
+
+DRIVER = r"""
+#include <cstdio>
+#include "item_order.hpp"
+int main() {
+  int BH, nb, mode, group, lead, ahead;
+  while (std::scanf("%d %d %d %d %d %d", &BH, &nb, &mode, &group, &lead, &ahead) == 6) {
+    for (int L = 0; L < BH * nb; ++L) {
+      int bh, i;
+      bsattn::map_item(L, BH, nb, mode, group, lead, ahead, bh, i);
+      std::printf("%d %d\n", bh, i);
+    }
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("order")
+    src = d / "order.cpp"
+    src.write_text(DRIVER)
+    exe = d / "order"
+    subprocess.run([gxx, "-O1", "-std=c++17", "-I", HDR, str(src), "-o", str(exe)], check=True)
+    return str(exe)
+
+
+def expected(BH, nb, mode, group, lead, ahead):
+    """The order by construction: a list per XCD, then item L = XCD L % 8's (L // 8)-th entry."""
+    if mode == 0:
+        return [(L % BH, nb - 1 - L // BH) for L in range(BH * nb)]
+    per_xcd = BH // 8
+    n = per_xcd // group
+    lead = min(lead, nb)
+    ahead = min(ahead, n) if lead > 0 else 0
+    out = [None] * (BH * nb)
+    for xcd in range(8):
+        def items(grp, ii_range):
+            return [(xcd + 8 * (grp * group + h), nb - 1 - ii) for ii in ii_range for h in range(group)]
+        seq = []
+        for grp in range(ahead):
+            seq += items(grp, range(lead))
+        for j in range(n):
+            if j + ahead < n and ahead > 0:
+                seq += items(j + ahead, range(lead))
+            seq += items(j, range(lead if ahead > 0 else 0, nb))
+        assert len(seq) == per_xcd * nb
+        for k, it in enumerate(seq):
+            out[8 * k + xcd] = it
+    return out
+
+
+CASES = []
+for BH in (8, 16, 64, 128, 256):
+    for nb in (1, 2, 3, 7, 64, 129):
+        per_xcd = BH // 8
+        for group in [g for g in range(1, per_xcd + 1) if per_xcd % g == 0][:4]:
+            for lead, ahead in ((0, 0), (2, 0), (0, 2), (1, 1), (2, 2), (2, 3), (4, 1), (300, 2), (2, 100)):
+                CASES.append((BH, nb, 1, group, lead, ahead))
+    for nb in (1, 5, 64):
+        CASES.append((BH, nb, 0, 1, 0, 0))
+CASES.append((24, 33, 0, 1, 0, 0))   # batch*heads not a multiple of 8: mode 0
+
+
+def test_order_is_the_constructed_one_and_a_bijection(driver):
+    stdin = "".join(" ".join(map(str, c)) + "\n" for c in CASES)
+    res = subprocess.run([driver], input=stdin, capture_output=True, text=True, check=True)
+    rows = [tuple(map(int, l.split())) for l in res.stdout.splitlines()]
+    pos = 0
+    for BH, nb, mode, group, lead, ahead in CASES:
+        got = rows[pos:pos + BH * nb]
+        pos += BH * nb
+        want = expected(BH, nb, mode, group, lead, ahead)
+        assert got == want, (BH, nb, mode, group, lead, ahead)
+        assert len(set(got)) == BH * nb   # every item exactly once
+        if mode == 1:
+            assert all(bh % 8 == L % 8 for L, (bh, _) in enumerate(got))
+    assert pos == len(rows)
+
+
+def test_heavy_rows_come_early(driver):
+    """B4 H32 with 128 query blocks, one head per group: without the look-ahead
+    the last head's two heaviest rows follow every row of the head before it;
+    with a look-ahead of two groups they precede the light rows of the head
+    three from the end."""
+    BH, nb, group = 128, 128, 1
+    n = BH // 8 // group
+
+    def xcd0(lead, ahead):
+        stdin = f"{BH} {nb} 1 {group} {lead} {ahead}\n"
+        res = subprocess.run([driver], input=stdin, capture_output=True, text=True, check=True)
+        seq = [tuple(map(int, l.split())) for l in res.stdout.splitlines()]
+        return [seq[8 * k] for k in range(BH * nb // 8)]
+
+    def pos(seq, head, rows):
+        return [k for k, (bh, i) in enumerate(seq) if bh == 8 * head and i in rows]
+
+    heavy, light = set(range(nb - 2, nb)), set(range(nb - 2))
+    plain = xcd0(0, 0)
+    assert min(pos(plain, n - 1, heavy)) > max(pos(plain, n - 2, light))
+    early = xcd0(2, 2)
+    assert max(pos(early, n - 1, heavy)) < min(pos(early, n - 3, light))
