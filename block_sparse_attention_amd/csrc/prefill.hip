@@ -733,13 +733,19 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   } else {
   constexpr int kHalf = C::kDT / 2;
   // KH: this wave's key half, as a compile-time value so o[] is indexed statically.
+  // The exchange area holds 16-byte pieces: piece (t, g4) of lane l, i.e.
+  // elements 4 g4 .. 4 g4 + 3 of the lane's tile t, at ((t * 4 + g4) * 64 + l) * 16.
   auto hand_over = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
-    float* xout = (float*)(smem + w * C::kXchgBytes);
+    unsigned char* xout = smem + w * C::kXchgBytes;
 #pragma unroll
     for (int t = 0; t < kHalf; ++t)
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) xout[(t * 16 + ii) * kWave + lane] = o[(1 - KH) * kHalf + t][ii];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& src = o[(1 - KH) * kHalf + t];
+        *(f32x4*)(xout + ((t * 4 + g4) * kWave + lane) * 16) =
+            f32x4{src[4 * g4], src[4 * g4 + 1], src[4 * g4 + 2], src[4 * g4 + 3]};
+      }
   };
   __syncthreads();   // the last block's V tile, read from a K slot, is done with
   if (kh == 0) hand_over(std::integral_constant<int, 0>{});
@@ -748,7 +754,7 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   stats[w * 2 * kWave + kWave + lane] = sum_with_half_swap(l);
   __syncthreads();
   const int pw = w ^ 2;   // partner: same rows, other key half
-  const float* xin = (const float*)(smem + pw * C::kXchgBytes);
+  const unsigned char* xin = smem + pw * C::kXchgBytes;
   const float m_b = stats[pw * 2 * kWave + lane];
   const float l_b = stats[pw * 2 * kWave + kWave + lane];
   const float l_a = sum_with_half_swap(l);
@@ -766,29 +772,42 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
   // contiguous in memory, so every wave store covers whole rows instead of
   // 8 bytes of 32 different rows (non-temporal: nothing here reads it again).
   unsigned char* const otile = smem + 2 * C::kTileBytes;
+  // The partner's pieces are all read first (one wait for the lot), and the
+  // uniform choice of destination is taken once, outside the loops.
   auto finish = [&](auto kh_c) {
     constexpr int KH = decltype(kh_c)::value;
-    const int r = 32 * rg + n;
+    constexpr int kBase = KH * kHalf;
+    f32x4 xb[kHalf][4];
 #pragma unroll
-    for (int t = 0; t < kHalf; ++t) {
-      constexpr int kBase = KH * kHalf;
+    for (int t = 0; t < kHalf; ++t)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float r4[4];
+      for (int g4 = 0; g4 < 4; ++g4)
+        xb[t][g4] = *(const f32x4*)(xin + ((t * 4 + g4) * kWave + lane) * 16);
+    auto merged = [&](int t, int g4, int e) {
+      return fmaf(o[kBase + t][4 * g4 + e], fa, xb[t][g4][e] * fb);
+    };
+    if (part >= 0) {
+      if (qrow < Sq) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ii = 4 * g4 + e;
-          r4[e] = o[kBase + t][ii] * fa + xin[(t * 16 + ii) * kWave + lane] * fb;
-        }
-        const int d = 32 * (kBase + t) + 8 * g4 + 4 * h;
-        if (part >= 0) {
-          if (qrow < Sq) *(float4*)(a.part_o + pr * D + d) = float4{r4[0], r4[1], r4[2], r4[3]};
-        } else {
-          const int g = d >> 3;
-          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ staged_swap<D>(r))) =
-              u32x2{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
-        }
+        for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = 32 * (kBase + t) + 8 * g4 + 4 * h;
+            *(float4*)(a.part_o + pr * D + d) = float4{merged(t, g4, 0), merged(t, g4, 1),
+                                                       merged(t, g4, 2), merged(t, g4, 3)};
+          }
       }
+    } else {
+      const int r = 32 * rg + n;
+#pragma unroll
+      for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int g = 4 * (kBase + t) + g4;   // 16-byte granule of d = 32 (kBase + t) + 8 g4
+          *(u32x2*)(otile + r * C::kRowBytes + (g ^ swz_k<D>(r)) * 16 + 8 * (h ^ staged_swap<D>(r))) =
+              u32x2{pack_bf16x2(merged(t, g4, 0), merged(t, g4, 1)),
+                    pack_bf16x2(merged(t, g4, 2), merged(t, g4, 3))};
+        }
     }
   };
   if (part >= 0 && qrow < Sq && kh == 0 && h == 0) a.part_ml[pr] = float2{M, lt};
