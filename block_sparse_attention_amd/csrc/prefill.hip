@@ -145,7 +145,8 @@ constexpr int kMaxKeyChunks = 4;   // fused row selection handles up to 256 key 
 
 template <int D, int KS, bool CAUSAL, int SRC>
 __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, int map_mode,
-                                                                  int group, int lead, int ahead) {
+                                                                  int group, int lead, int ahead,
+                                                                  int tail) {
   using C = Cfg<D, KS>;
   constexpr int kWaves = C::kWaves;
   constexpr int NT = C::NT;
@@ -177,10 +178,11 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       (kCanSplit && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
   const bool helper = (int)blockIdx.x < n_help;
   if (helper) {
-    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, 0, 0, bh, i);
+    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, 0, 0, false, bh, i);
     i += a.split_row0;
   } else {
-    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, lead, ahead, bh, i);
+    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, lead, ahead, tail != 0, bh,
+             i);
   }
 
   const int64_t q_off = (int64_t)bh * Sq * D;
@@ -910,26 +912,26 @@ template <int D, int KS, bool CAUSAL, int SRC>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   // Item order (item_order.hpp).  Heads per group: as many as one XCD's
-  // 4 MB L2 holds the K/V of, but at least two: with one head per group a
-  // dense last row (~110 us at B4 H32 S8192 D128) outlasts its head's turn
-  // and the last head's rows trail the launch (two per group measured 2%
-  // faster there, 3.5% at B1 H32 S16384 D128).  At D = 64 the two heaviest
-  // rows of each group are also issued two groups early (6% faster at B4
-  // H32 S8192 D64); at D = 128 that measured no faster, since those rows
-  // then find their K/V outside the L2 the current group fills.
-  int mode = 0, group = 1, lead = 0, ahead = 0;
+  // 4 MB L2 holds the K/V of.  A dense last row (~110 us at B4 H32 S8192
+  // D128) outlasts one group's turn, so the last group's rows would trail
+  // the launch: at D = 128 the last group's two heaviest rows are issued
+  // four groups early (3.5% faster at B1 H32 S16384 D128, 3% at B4 H32
+  // S8192 D128, with the L2 hit rate of the plain walk); at D = 64 every
+  // group's two heaviest rows go two groups early (6% faster at B4 H32
+  // S8192 D64; at D = 128 that measured no faster, since those rows then
+  // find their K/V outside the L2 the current group fills).
+  int mode = 0, group = 1, lead = 0, ahead = 0, tail = 0;
   if (BH % 8 == 0) {
     mode = 1;
     const int per_xcd = BH / 8;
     const double kv_bytes = 2.0 * a.Sk * D * 2.0;
-    int g = max(2, (int)(4.0 * 1024 * 1024 / kv_bytes));
+    int g = (int)(4.0 * 1024 * 1024 / kv_bytes);
     g = max(1, min(g, per_xcd));
     while (per_xcd % g) --g;
     group = g;
-    if (D == 64) {
-      lead = 2;
-      ahead = 2;
-    }
+    lead = 2;
+    ahead = D == 64 ? 2 : 4;
+    tail = D == 64 ? 0 : 1;
   }
   const size_t lds = lds_bytes<D, KS>(a.nbk);
   auto kern = prefill_kernel<D, KS, CAUSAL, SRC>;
@@ -945,7 +947,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
       (SRC != kSrcList && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
   const int64_t items = (int64_t)BH * a.nbq + slots;
   hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
-                     group, lead, ahead);
+                     group, lead, ahead, tail);
   if (slots > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

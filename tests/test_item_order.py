@@ -3,10 +3,12 @@
 map_item must be a bijection from work-group index to (batch*head, query
 block); in mode 1 each item must run on the XCD that owns its head
 (bh % 8 == L % 8); and the order must be the one the header describes, which
-this test builds independently by concatenating lists: per XCD, the heavy
-items (the first `lead` query blocks, descending) of groups 0 .. ahead-1,
-then for each group j the heavy items of group j + ahead followed by group
-j's remaining query blocks, heads interleaved within a group."""
+this test builds independently by concatenating lists: per XCD, either the
+heavy items (the first `lead` query blocks, descending) of groups 0 ..
+ahead-1, then for each group j the heavy items of group j + ahead followed
+by group j's remaining query blocks; or (tail) the plain walk with only the
+last group's heavy items moved to just before group n - 1 - ahead; heads
+interleaved within a group."""
 import os
 import shutil
 import subprocess
@@ -20,11 +22,11 @@ DRIVER = r"""
 #include <cstdio>
 #include "item_order.hpp"
 int main() {
-  int BH, nb, mode, group, lead, ahead;
-  while (std::scanf("%d %d %d %d %d %d", &BH, &nb, &mode, &group, &lead, &ahead) == 6) {
+  int BH, nb, mode, group, lead, ahead, tail;
+  while (std::scanf("%d %d %d %d %d %d %d", &BH, &nb, &mode, &group, &lead, &ahead, &tail) == 7) {
     for (int L = 0; L < BH * nb; ++L) {
       int bh, i;
-      bsattn::map_item(L, BH, nb, mode, group, lead, ahead, bh, i);
+      bsattn::map_item(L, BH, nb, mode, group, lead, ahead, tail != 0, bh, i);
       std::printf("%d %d\n", bh, i);
     }
   }
@@ -46,25 +48,34 @@ def driver(tmp_path_factory):
     return str(exe)
 
 
-def expected(BH, nb, mode, group, lead, ahead):
+def expected(BH, nb, mode, group, lead, ahead, tail):
     """The order by construction: a list per XCD, then item L = XCD L % 8's (L // 8)-th entry."""
     if mode == 0:
         return [(L % BH, nb - 1 - L // BH) for L in range(BH * nb)]
     per_xcd = BH // 8
     n = per_xcd // group
     lead = min(lead, nb)
-    ahead = min(ahead, n) if lead > 0 else 0
+    ahead = min(ahead, n - 1 if tail else n)
+    if lead <= 0 or ahead <= 0:
+        lead = ahead = 0
     out = [None] * (BH * nb)
     for xcd in range(8):
         def items(grp, ii_range):
             return [(xcd + 8 * (grp * group + h), nb - 1 - ii) for ii in ii_range for h in range(group)]
         seq = []
-        for grp in range(ahead):
-            seq += items(grp, range(lead))
-        for j in range(n):
-            if j + ahead < n and ahead > 0:
-                seq += items(j + ahead, range(lead))
-            seq += items(j, range(lead if ahead > 0 else 0, nb))
+        if tail:
+            for j in range(n - 1):
+                if j == n - 1 - ahead:
+                    seq += items(n - 1, range(lead))
+                seq += items(j, range(nb))
+            seq += items(n - 1, range(lead, nb) if ahead else range(nb))
+        else:
+            for grp in range(ahead):
+                seq += items(grp, range(lead))
+            for j in range(n):
+                if j + ahead < n and ahead > 0:
+                    seq += items(j + ahead, range(lead))
+                seq += items(j, range(lead, nb))
         assert len(seq) == per_xcd * nb
         for k, it in enumerate(seq):
             out[8 * k + xcd] = it
@@ -77,10 +88,11 @@ for BH in (8, 16, 64, 128, 256):
         per_xcd = BH // 8
         for group in [g for g in range(1, per_xcd + 1) if per_xcd % g == 0][:4]:
             for lead, ahead in ((0, 0), (2, 0), (0, 2), (1, 1), (2, 2), (2, 3), (4, 1), (300, 2), (2, 100)):
-                CASES.append((BH, nb, 1, group, lead, ahead))
+                for tail in (0, 1):
+                    CASES.append((BH, nb, 1, group, lead, ahead, tail))
     for nb in (1, 5, 64):
-        CASES.append((BH, nb, 0, 1, 0, 0))
-CASES.append((24, 33, 0, 1, 0, 0))   # batch*heads not a multiple of 8: mode 0
+        CASES.append((BH, nb, 0, 1, 0, 0, 0))
+CASES.append((24, 33, 0, 1, 0, 0, 0))   # batch*heads not a multiple of 8: mode 0
 
 
 def test_order_is_the_constructed_one_and_a_bijection(driver):
@@ -88,11 +100,11 @@ def test_order_is_the_constructed_one_and_a_bijection(driver):
     res = subprocess.run([driver], input=stdin, capture_output=True, text=True, check=True)
     rows = [tuple(map(int, l.split())) for l in res.stdout.splitlines()]
     pos = 0
-    for BH, nb, mode, group, lead, ahead in CASES:
+    for BH, nb, mode, group, lead, ahead, tail in CASES:
         got = rows[pos:pos + BH * nb]
         pos += BH * nb
-        want = expected(BH, nb, mode, group, lead, ahead)
-        assert got == want, (BH, nb, mode, group, lead, ahead)
+        want = expected(BH, nb, mode, group, lead, ahead, tail)
+        assert got == want, (BH, nb, mode, group, lead, ahead, tail)
         assert len(set(got)) == BH * nb   # every item exactly once
         if mode == 1:
             assert all(bh % 8 == L % 8 for L, (bh, _) in enumerate(got))
@@ -107,8 +119,8 @@ def test_heavy_rows_come_early(driver):
     BH, nb, group = 128, 128, 1
     n = BH // 8 // group
 
-    def xcd0(lead, ahead):
-        stdin = f"{BH} {nb} 1 {group} {lead} {ahead}\n"
+    def xcd0(lead, ahead, tail=0):
+        stdin = f"{BH} {nb} 1 {group} {lead} {ahead} {tail}\n"
         res = subprocess.run([driver], input=stdin, capture_output=True, text=True, check=True)
         seq = [tuple(map(int, l.split())) for l in res.stdout.splitlines()]
         return [seq[8 * k] for k in range(BH * nb // 8)]
@@ -121,3 +133,9 @@ def test_heavy_rows_come_early(driver):
     assert min(pos(plain, n - 1, heavy)) > max(pos(plain, n - 2, light))
     early = xcd0(2, 2)
     assert max(pos(early, n - 1, heavy)) < min(pos(early, n - 3, light))
+    # tail only: the last head's heavy rows just before head n - 5; every other head in plain order
+    tail = xcd0(2, 4, 1)
+    assert max(pos(tail, n - 6, light)) < min(pos(tail, n - 1, heavy))
+    assert max(pos(tail, n - 1, heavy)) < min(pos(tail, n - 5, light | heavy))
+    for h in range(n - 1):
+        assert pos(tail, h, heavy | light) == pos(plain, h, heavy | light) or h >= n - 5
