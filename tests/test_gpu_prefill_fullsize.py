@@ -8,7 +8,9 @@ four of its rows — the first and last row of each 32-row wave group — so
 every work-group, split halves included, meets the oracle (the block-sparse
 guide's §5 reference check, restricted to rows the oracle computes one by
 one).  The fused one-launch forms run on the same workloads and meet the
-oracle on the same rows; their mask output is byte-exact."""
+oracle on the same rows; their mask output is byte-exact.  A third workload,
+B1 H32 S8192 D64 (top-32, dense last two rows), runs the D = 64 issue order
+in which every head group's two heaviest rows go out two groups early."""
 import functools
 
 import numpy as np
@@ -31,10 +33,15 @@ def _rows(S):
     return np.array([64 * i + r for i in range(nb) for r in ROWS_IN_BLOCK if 64 * i + r < S], np.int64)
 
 
+# four heads per XCD, two per group (2 MiB of K/V each at S8192 D64): two
+# groups, so the look-ahead order is the one that runs
+D64 = gen.custom_prefill(1, 32, 8192, 64, "topk", topk=32, dense_last_two_rows=True, qkv_scale=0.5)
+
+
 @functools.lru_cache(maxsize=2)
 def _case(name):
     """Inputs, the oracle's mask and the oracle's rows for every (b, h)."""
-    cfg = gen.CONFIGS[name]
+    cfg = D64 if name == "D64" else gen.CONFIGS[name]
     inp = gen.prefill_inputs(cfg, 0)
     if cfg.mask_kind == "topk":
         mask = om.build_mask_topk(inp["scores"], cfg.topk, cfg.dense_last_two_rows, cfg.force_diagonal)
@@ -59,7 +66,7 @@ def _gather(out, rows):
     return gpu_bf16_to_f64(out.index_select(2, idx))
 
 
-@pytest.mark.parametrize("name", ["C3", "C4"])
+@pytest.mark.parametrize("name", ["C3", "C4", "D64"])
 def test_every_work_item_two_launch_path(name):
     cfg, inp, mask, rows, want = _case(name)
     say(f"[prefill-full] {name} builder + bsattn_fwd, B{cfg.B} H{cfg.H} S{cfg.S} D{cfg.D}")
