@@ -144,9 +144,8 @@ struct Probs {
 constexpr int kMaxKeyChunks = 4;   // fused row selection handles up to 256 key blocks
 
 template <int D, int KS, bool CAUSAL, int SRC>
-__global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, int map_mode,
-                                                                  int group, int lead, int ahead,
-                                                                  int tail) {
+__global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a, ItemOrder items,
+                                                                  ItemOrder helpers) {
   using C = Cfg<D, KS>;
   constexpr int kWaves = C::kWaves;
   constexpr int NT = C::NT;
@@ -178,11 +177,10 @@ __global__ __launch_bounds__(kThreadsFor<KS>) void prefill_kernel(PrefillArgs a,
       (kCanSplit && a.split_min > 0) ? a.B * a.H * (nbq - a.split_row0) : 0;
   const bool helper = (int)blockIdx.x < n_help;
   if (helper) {
-    map_item(blockIdx.x, a.B * a.H, nbq - a.split_row0, map_mode, group, 0, 0, false, bh, i);
+    map_item(helpers, blockIdx.x, bh, i);
     i += a.split_row0;
   } else {
-    map_item((int)blockIdx.x - n_help, a.B * a.H, nbq, map_mode, group, lead, ahead, tail != 0, bh,
-             i);
+    map_item(items, (int)blockIdx.x - n_help, bh, i);
   }
 
   const int64_t q_off = (int64_t)bh * Sq * D;
@@ -946,8 +944,13 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t slots =
       (SRC != kSrcList && a.split_min > 0) ? (int64_t)BH * (a.nbq - a.split_row0) : 0;
   const int64_t items = (int64_t)BH * a.nbq + slots;
-  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, mode,
-                     group, lead, ahead, tail);
+  // the issue orders of the items and of the long rows' helpers, every
+  // quotient they need computed here
+  const ItemOrder order = make_item_order(BH, a.nbq, mode, group, lead, ahead, tail != 0);
+  const ItemOrder help_order =
+      slots > 0 ? make_item_order(BH, a.nbq - a.split_row0, mode, group, 0, 0, false) : ItemOrder{};
+  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(Cfg<D, KS>::kThreads), lds, stream, a, order,
+                     help_order);
   if (slots > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

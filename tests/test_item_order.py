@@ -35,6 +35,59 @@ int main() {
 """
 
 
+DIV_DRIVER = r"""
+#include <cstdio>
+#include "item_order.hpp"
+int main() {
+  unsigned d, x;
+  while (std::scanf("%u %u", &d, &x) == 2) {
+    const bsattn::FastDiv f = bsattn::make_fastdiv(d);
+    std::printf("%d\n", bsattn::fdiv((int)x, f));
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def div_driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("fdiv")
+    src = d / "fdiv.cpp"
+    src.write_text(DIV_DRIVER)
+    exe = d / "fdiv"
+    subprocess.run([gxx, "-O1", "-std=c++17", "-I", HDR, str(src), "-o", str(exe)], check=True)
+    return str(exe)
+
+
+def test_fast_division_is_exact(div_driver):
+    """The launch-time divisors' multiply-and-shift quotient equals integer
+    division for every dividend in [0, 2^31): checked at the edges (0, 1,
+    multiples of d and their neighbours, 2^31 - 1) and on seeded random
+    dividends, for every divisor up to 4096 and for large and power-of-two
+    divisors."""
+    import random
+    rng = random.Random(0)
+    top = 2 ** 31 - 1
+    divisors = list(range(1, 4097)) + [2 ** k for k in range(13, 31)] + [2 ** k + 1 for k in range(13, 31)] \
+        + [2 ** k - 1 for k in range(13, 32)] + [rng.randrange(4097, top) for _ in range(300)]
+    pairs = []
+    for d in divisors:
+        xs = {0, 1, d - 1, d, d + 1, top, top - 1, top - (top % d), top - (top % d) - 1}
+        q = top // d
+        xs |= {q * d, max(0, q * d - 1), (q // 2) * d - 1 if q >= 2 else 0}
+        xs |= {rng.randrange(0, top + 1) for _ in range(20)}
+        pairs += [(d, x) for x in xs if 0 <= x <= top]
+    stdin = "".join(f"{d} {x}\n" for d, x in pairs)
+    res = subprocess.run([div_driver], input=stdin, capture_output=True, text=True, check=True)
+    got = list(map(int, res.stdout.split()))
+    assert len(got) == len(pairs)
+    bad = [(d, x, g) for (d, x), g in zip(pairs, got) if g != x // d]
+    assert not bad, bad[:5]
+
+
 @pytest.fixture(scope="module")
 def driver(tmp_path_factory):
     gxx = shutil.which("g++")
@@ -93,6 +146,8 @@ for BH in (8, 16, 64, 128, 256):
     for nb in (1, 5, 64):
         CASES.append((BH, nb, 0, 1, 0, 0, 0))
 CASES.append((24, 33, 0, 1, 0, 0, 0))   # batch*heads not a multiple of 8: mode 0
+CASES.append((32, 256, 1, 1, 2, 4, 1))  # B1 H32 S16384: the long-row workload's order
+CASES.append((32, 128, 1, 1, 0, 0, 0))  # its long rows' helpers (query blocks 128 .. 255)
 
 
 def test_order_is_the_constructed_one_and_a_bijection(driver):
