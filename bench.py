@@ -63,15 +63,21 @@ HBM_PEAK_GBPS = 8000.0        # 8 TB/s HBM3E
 FLOP_PER_BLOCK = lambda D: 4 * 64 * 64 * D   # QK^T and PV on one 64x64 block pair
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+_CSRC = os.path.join(ROOT, "block_sparse_attention_amd", "csrc")
+# the sources a kernel's counters depend on (the forward's issue order lives in a header)
 KERNEL_SRC = {
-    "prefill": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "prefill.hip"),
-    "decode": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "decode.hip"),
-    "xattn": os.path.join(ROOT, "block_sparse_attention_amd", "csrc", "xattn.hip"),
+    "prefill": [os.path.join(_CSRC, "prefill.hip"), os.path.join(_CSRC, "item_order.hpp")],
+    "decode": [os.path.join(_CSRC, "decode.hip")],
+    "xattn": [os.path.join(_CSRC, "xattn.hip")],
 }
 
 
-def _sha(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def _sha(paths) -> str:
+    """sha256 of one source, or of several sources' bytes one after another."""
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
 
 
 def _traffic(kernel: str, workload: str):
