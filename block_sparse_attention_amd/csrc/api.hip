@@ -166,6 +166,7 @@ bsattn_status bsattn_build_mask_threshold(const float* scores, int B, int H, int
                                           bsattn_stream_t stream) {
   if (!scores || !mask) return BSATTN_ERR_NULL;
   if (B <= 0 || H <= 0 || nb <= 0) return BSATTN_ERR_SHAPE;
+  if (prod3(B, H, nb) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
   return launch_mask_threshold(scores, B, H, nb, threshold, dense_last_two_rows ? 1 : 0,
                                force_diagonal ? 1 : 0, mask, as_hip(stream)) == hipSuccess
              ? BSATTN_OK

@@ -74,7 +74,8 @@ const char* bsattn_version(void);
  * then every column j > i is cleared (tril); then, if force_diagonal, the
  * diagonal block is set (the causal diagonal block is always kept in the
  * XAttention guide, "algorithm flow", phase 3).
- * Errors: NULL pointers; B, H, nb <= 0 or topk < 0 or topk > nb (SHAPE).
+ * Errors: NULL pointers; B, H, nb <= 0, topk < 0 or topk > nb, or more than
+ * 2^31 - 1 rows B*H*nb (SHAPE).
  */
 bsattn_status bsattn_build_mask_topk(const float* scores, int B, int H, int nb, int topk,
                                      int dense_last_two_rows, int force_diagonal, uint8_t* mask,
@@ -84,7 +85,8 @@ bsattn_status bsattn_build_mask_topk(const float* scores, int B, int H, int nb, 
  * Threshold block mask (same guide, §3.2): a block is selected when its score
  * is strictly greater than `threshold`; then the same dense-last-two-rows,
  * tril and diagonal steps as bsattn_build_mask_topk.
- * Errors: NULL pointers; B, H, nb <= 0 (SHAPE).
+ * Errors: NULL pointers; B, H, nb <= 0 or more than 2^31 - 1 rows B*H*nb
+ * (SHAPE).
  */
 bsattn_status bsattn_build_mask_threshold(const float* scores, int B, int H, int nb,
                                           float threshold, int dense_last_two_rows,
@@ -98,7 +100,8 @@ bsattn_status bsattn_build_mask_threshold(const float* scores, int B, int H, int
  *   idx  : int32 [B, H, nb, nb]; row (b,h,i) lists ascending every j with
  *          mask != 0 (and j <= i when is_causal), then -1 padding.
  *   cnt  : int32 [B, H, nb], the list lengths.
- * Errors: NULL pointers; B, H, nb <= 0 (SHAPE).
+ * Errors: NULL pointers; B, H, nb <= 0, or more rows B*H*nb than one launch
+ * covers (four rows per work-group, at most 2^31 - 1 work-groups) (SHAPE).
  */
 bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, int is_causal,
                                      int32_t* idx, int32_t* cnt, bsattn_stream_t stream);

@@ -50,6 +50,10 @@ def test_mask_builders_validate_on_host():
     assert lib.bsattn_build_mask_topk(FAKE, 0, 1, 4, 1, 0, 1, FAKE, None) == 2
     assert lib.bsattn_build_mask_threshold(FAKE, 1, 1, 0, 0.5, 0, 1, FAKE, None) == 2
     assert lib.bsattn_build_mask_threshold(FAKE, 1, 1, 4, 0.5, 0, 1, None, None) == 1
+    # more than 2^31 - 1 rows
+    assert lib.bsattn_build_mask_topk(FAKE, 65536, 65536, 1, 1, 0, 1, FAKE, None) == 2
+    assert lib.bsattn_build_mask_threshold(FAKE, 65536, 65536, 1, 0.5, 0, 1, FAKE, None) == 2
+    assert lib.bsattn_mask_to_indices(FAKE, 65536, 65536, 4, 1, FAKE, FAKE, None) == 2
     assert lib.bsattn_mask_to_indices(FAKE, 1, -1, 4, 1, FAKE, FAKE, None) == 2
     assert lib.bsattn_mask_to_indices(FAKE, 1, 1, 4, 1, None, FAKE, None) == 1
 
