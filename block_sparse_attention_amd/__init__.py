@@ -18,8 +18,8 @@ from typing import Optional, Tuple
 __all__ = [
     "BLOCK", "BsattnError", "load_library", "bsattn_status_string", "bsattn_version",
     "bsattn_build_mask_topk", "bsattn_build_mask_threshold", "bsattn_mask_to_indices",
-    "bsattn_fwd_workspace_bytes", "bsattn_fwd", "bsattn_fwd_indices", "bsattn_fwd_chunk",
-    "bsattn_fwd_topk", "bsattn_fwd_threshold",
+    "bsattn_fwd_workspace_bytes", "bsattn_fwd_max_key_blocks", "bsattn_fwd", "bsattn_fwd_indices",
+    "bsattn_fwd_chunk", "bsattn_fwd_topk", "bsattn_fwd_threshold",
     "bsattn_decode_num_splits", "bsattn_decode_default_splits", "bsattn_decode_workspace_bytes",
     "bsattn_decode_gqa", "bsattn_decode_gqa_noalloc", "bsattn_decode_noalloc_scratch_bytes",
     "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged",
@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "bsattn_decode_gqa_mask", "bsattn_decode_gqa_paged", "bsattn_fwd_chunk",
     "bsattn_fwd_topk", "bsattn_fwd_threshold", "bsattn_xattn_workspace_bytes",
     "bsattn_xattn_block_sums", "bsattn_build_mask_cumulative", "bsattn_xattn_estimate",
-    "bsattn_decode_gqa_noalloc", "bsattn_decode_noalloc_scratch_bytes",
+    "bsattn_decode_gqa_noalloc", "bsattn_decode_noalloc_scratch_bytes", "bsattn_fwd_max_key_blocks",
 )
 
 _STATUS = {0: "BSATTN_OK", 1: "BSATTN_ERR_NULL", 2: "BSATTN_ERR_SHAPE",
@@ -65,6 +65,7 @@ _SIGS = {
     "bsattn_build_mask_threshold": (_I, [_P, _I, _I, _I, _F, _I, _I, _P, _P]),
     "bsattn_mask_to_indices": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bsattn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "bsattn_fwd_max_key_blocks": (_I, [_I]),
     "bsattn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "bsattn_fwd_indices": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "bsattn_fwd_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
@@ -215,6 +216,11 @@ def bsattn_mask_to_indices(mask, is_causal: bool = True, idx=None, cnt=None,
 
 def bsattn_fwd_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
     return int(load_library().bsattn_fwd_workspace_bytes(B, H, S, D))
+
+
+def bsattn_fwd_max_key_blocks(D: int) -> int:
+    """Most key blocks ceil(Sk/64) a forward call takes at head dim D (0: D unsupported)."""
+    return int(load_library().bsattn_fwd_max_key_blocks(D))
 
 
 def _qkv(q, k, v):

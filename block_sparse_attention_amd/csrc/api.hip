@@ -189,14 +189,29 @@ size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D) {
   return split_layout(B, H, nblocks(S), D).bytes;
 }
 
+// Block lists are held as 16-bit entries in LDS next to the K/V ring.
+static bool fwd_key_blocks_ok(int D, int nbk) {
+  return nbk <= 65535 && prefill_lds_bytes(D, nbk) <= kMaxLdsBytes;
+}
+
+int bsattn_fwd_max_key_blocks(int D) {
+  if (!head_dim_ok(D)) return 0;
+  int lo = 1, hi = 65535;   // the LDS use grows with nbk: bisect for the last that fits
+  if (!fwd_key_blocks_ok(D, lo)) return 0;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (fwd_key_blocks_ok(D, mid)) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // The shape checks every forward form shares.
 static bsattn_status fwd_check(int B, int H, int Sq, int Sk, int D) {
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk < Sq) return BSATTN_ERR_SHAPE;
   if (!head_dim_ok(D)) return BSATTN_ERR_UNSUPPORTED;
   if (prod3(B, H, nblocks(Sq)) > 0x7fffffffLL) return BSATTN_ERR_SHAPE;
-  // block lists are held as 16-bit entries in LDS next to the K/V ring
-  if (nblocks(Sk) > 65535 || prefill_lds_bytes(D, nblocks(Sk)) > kMaxLdsBytes)
-    return BSATTN_ERR_UNSUPPORTED;
+  if (!fwd_key_blocks_ok(D, nblocks(Sk))) return BSATTN_ERR_UNSUPPORTED;
   if (!fits_elems((long double)B * H * Sk * D)) return BSATTN_ERR_SHAPE;
   return BSATTN_OK;
 }

@@ -133,8 +133,9 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
  * workspace: device memory of bsattn_fwd_workspace_bytes bytes, 16-byte
  * aligned, used by causal calls only (may be NULL when that size is 0);
  * calls that overlap in time need workspaces of their own.
- * Errors: NULL pointers; B, H, S <= 0 (SHAPE); D not 64 or 128 (UNSUPPORTED);
- * workspace NULL, misaligned or below bsattn_fwd_workspace_bytes (WORKSPACE).
+ * Errors: NULL pointers; B, H, S <= 0 (SHAPE); D not 64 or 128, or
+ * ceil(S/64) above bsattn_fwd_max_key_blocks(D) (UNSUPPORTED); workspace
+ * NULL, misaligned or below bsattn_fwd_workspace_bytes (WORKSPACE).
  */
 /* Workspace of bsattn_fwd (and of the fused bsattn_fwd_topk and
  * bsattn_fwd_threshold): nonzero when S spans more than 128 key blocks
@@ -143,6 +144,13 @@ bsattn_status bsattn_mask_to_indices(const uint8_t* mask, int B, int H, int nb, 
  * 256-byte aligned); 0 when no row can split, when the split would need more
  * than 2 GiB (such calls then run unsplit), or for arguments out of range. */
 size_t bsattn_fwd_workspace_bytes(int B, int H, int S, int D);
+
+/* The most key blocks (ceil(Sk/64)) a forward call takes at head dim D: each
+ * work item holds its ascending active-block list in on-chip memory beside
+ * its K/V tiles, 2 bytes per block.  0 for a head dim the forward does not
+ * take.  Every forward form (bsattn_fwd, _indices, _chunk, _topk,
+ * _threshold) returns UNSUPPORTED above it. */
+int bsattn_fwd_max_key_blocks(int D);
 
 bsattn_status bsattn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint8_t* block_mask, int B, int H, int S, int D, int is_causal,
@@ -203,7 +211,7 @@ bsattn_status bsattn_fwd_threshold(const uint16_t* q, const uint16_t* k, const u
  * PAST_LEN).  Keys at or past Sk are masked; rows with no visible key output
  * 0.  Sq = Sk is bsattn_fwd.  Needs no workspace.
  * Errors: NULL pointers; B, H, Sq <= 0 or Sk < Sq (SHAPE); D not 64 or 128,
- * or ceil(Sk/64) too large for the on-chip block list (UNSUPPORTED).
+ * or ceil(Sk/64) above bsattn_fwd_max_key_blocks(D) (UNSUPPORTED).
  */
 bsattn_status bsattn_fwd_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const uint8_t* block_mask, int B, int H, int Sq, int Sk, int D,

@@ -215,6 +215,22 @@ def test_chunk_fwd_validates_on_host():
     assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 64, 128, 96, 1, F, None) == 3
 
 
+def test_fwd_key_block_limit_on_host():
+    """The longest key range each head dim takes: every forward form refuses
+    one block more before any launch (UNSUPPORTED)."""
+    lib = _lib()
+    F = FAKE
+    assert lib.bsattn_fwd_max_key_blocks(96) == 0
+    m64, m128 = lib.bsattn_fwd_max_key_blocks(64), lib.bsattn_fwd_max_key_blocks(128)
+    assert 256 < m128 < m64 <= 65535, (m64, m128)   # D = 128 holds a larger K/V ring
+    for D, m in ((64, m64), (128, m128)):
+        Sk = (m + 1) * 64
+        assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 64, Sk, D, 1, F, None) == 3
+        assert lib.bsattn_fwd_chunk(F, F, F, F, 1, 1, 64, Sk - 63, D, 0, F, None) == 3  # ragged tail
+        assert lib.bsattn_fwd(F, F, F, F, 1, 1, Sk, D, 0, F, None, 0, None) == 3
+        assert lib.bsattn_fwd_indices(F, F, F, F, F, 1, 1, Sk, D, 0, F, None) == 3
+
+
 def test_mask_form_decode_validates_on_host():
     lib = _lib()
     F = FAKE

@@ -110,3 +110,60 @@ def test_chunk_large_sampled_rows():
     for h in (0, 5):
         want = oa.prefill_head_rows(f(q[0, h]), f(k[0, h]), f(v[0, h]), m[0, h], True, rows)
         check_close(got[0, h, rows], want, f"large chunk h{h}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ragged", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_longest_key_range(D, ragged, causal):
+    """The longest key range the forward takes (bsattn_fwd_max_key_blocks:
+    64511 key blocks at D 64, 48127 at D 128, about 4.1 M and 3.1 M tokens),
+    one 64-query chunk at its end.  Every key block the mask leaves out holds
+    NaN on the device, so a read of any of them into the result shows up as
+    a non-finite output.  The expected rows come from the oracle on the
+    selected blocks alone, laid end to end: every selected block before the
+    last two is fully visible to every query row in both problems, and the
+    last two (always selected) keep their offsets from the end of the keys,
+    so each row sees the same keys at the same causal positions."""
+    nbk = bsa.bsattn_fwd_max_key_blocks(D)
+    assert nbk > 0
+    Sk = nbk * 64 - (13 if ragged else 0)
+    Sq, H = 64, 2
+    rng = np.random.default_rng(nbk + 2 * ragged + causal)
+    fixed = [{0, 1, 63, 64, 255, 256, 4095, 4096, nbk // 2, nbk - 66, nbk - 65, nbk - 64},
+             {0}]
+    sel = []
+    for h in range(H):
+        s = set(fixed[h]) | {nbk - 2, nbk - 1}
+        if h == 0:
+            s |= set(rng.integers(0, nbk - 2, 20).tolist())
+        sel.append(sorted(s))
+    q = gen.f32_to_bf16_bits(rng.standard_normal((1, H, Sq, D), dtype=np.float32))
+    nan = float("nan")
+    k_dev = torch.full((1, H, Sk, D), nan, dtype=torch.bfloat16, device="cuda")
+    v_dev = torch.full((1, H, Sk, D), nan, dtype=torch.bfloat16, device="cuda")
+    m = np.zeros((1, H, 1, nbk), np.uint8)
+    kc, vc = [], []   # per head: the selected blocks' rows laid end to end
+    for h in range(H):
+        m[0, h, 0, sel[h]] = 1
+        n_rows = sum(min(64, Sk - 64 * j) for j in sel[h])
+        kh = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, D), dtype=np.float32))
+        vh = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, D), dtype=np.float32))
+        pos = 0
+        for j in sel[h]:
+            n = min(64, Sk - 64 * j)
+            k_dev[0, h, 64 * j:64 * j + n] = to_gpu_bf16(kh[pos:pos + n])
+            v_dev[0, h, 64 * j:64 * j + n] = to_gpu_bf16(vh[pos:pos + n])
+            pos += n
+        kc.append(kh)
+        vc.append(vh)
+    say(f"[prefill-chunk] longest key range D={D} nbk={nbk} Sk={Sk} causal={causal} "
+        f"blocks={[len(s) for s in sel]}")
+    got = gpu_bf16_to_f64(bsa.bsattn_fwd_chunk(to_gpu_bf16(q), k_dev, v_dev, to_gpu(m), causal))
+    del k_dev, v_dev
+    torch.cuda.empty_cache()
+    f = gen.bf16_bits_to_f64
+    for h in range(H):
+        ones = np.ones((1, len(sel[h])), np.uint8)
+        want = oa.prefill_head_rows(f(q[0, h]), f(kc[h]), f(vc[h]), ones, causal)
+        check_close(got[0, h], want, f"longest key range D{D} ragged{ragged} c{causal} h{h}")
