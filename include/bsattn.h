@@ -24,6 +24,10 @@
  * reported by the HIP runtime returns BSATTN_ERR_HIP.  Data content is never
  * an error: a nonzero mask byte means "selected", a block index outside the
  * valid range selects nothing; non-finite scores give unspecified masks.
+ * Only the keys and values of selected blocks (and, in decode, of rows
+ * before each sequence's end) are read: anything, NaN included, may sit in
+ * the rest.  What is read must be finite; a NaN or infinity there gives
+ * unspecified outputs.
  *
  * The block size is fixed at 64 tokens (BSATTN_BLOCK) for both the query and
  * the key/value dimension, as in the TileLang block-sparse Flash-Attention
