@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running parity case at full workload size")
+    # A planted oracle mistake for the run (tests/test_oracle_mutants.py sets it
+    # in the child runs it starts; never set in a normal run).
+    mutant = os.environ.get("BSATTN_ORACLE_MUTANT")
+    if mutant:
+        from tests import oracle_mutants
+        oracle_mutants.apply(mutant)
 
 
 def pytest_collection_modifyitems(config, items):

@@ -15,7 +15,7 @@ def test_worked_values():
         tm, sms, nn, nm, size, causal, mx, want = (int(x) for x in line.split())
         assert oh.num_splits_heuristic(tm, sms, nn, nm, size, bool(causal), mx) == want, line
         n += 1
-    assert n == 9
+    assert n == 10
 
 
 def test_decode_wrapper_on_the_decode_workload():
