@@ -13,8 +13,9 @@ query row r of head (b, h):
     s_t = (q_r . k_t) / sqrt(D)          over allowed t
     O_r = sum_t softmax(s)_t v_t,        O_r = 0 when no t is allowed.
 
-The in-block causal rule (key t visible iff t <= r) is the guide's §4.5
-reading of "0 below the diagonal, -inf above it"; the empty-row value 0 is
+The in-block causal rule (key t visible iff t <= r) reads the guide's §4.5
+in-block mask, which adds zero on and below the diagonal and minus infinity
+above it; the empty-row value 0 is
 the reading for rows that hit no block (the guide relies on exp2(-inf) = 0
 and never forms such a row in its test).  The online softmax of §4.6 is a
 re-association of exactly this sum, so the oracle does not reproduce it.

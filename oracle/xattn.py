@@ -31,10 +31,11 @@ Readings (the page leaves these open or states them inconsistently):
   rows and columns (the page's sparse kernel fixes 128 for its own library).
 * selection keeps a column while the weight ranked above it (the exclusive
   cumulative sum) is still below the required mass, i.e. the smallest ranked
-  prefix that reaches it.  This is what the flow chart's "accumulate until
-  >= threshold * total" and the worked example (row 0.05 0.30 0.40 0.15 0.10
-  at 0.9 keeps four blocks) say; the listing's ``cumsum < required`` would
-  keep three there.
+  prefix that reaches it.  This is what the flow chart (weights added until
+  they reach the threshold's share of the total) and the worked example (row
+  0.05 0.30 0.40 0.15 0.10 at 0.9 keeps four blocks) say; testing the
+  inclusive cumulative sum against the required mass, as the listing does,
+  would keep three there.
 * the total includes the kept sink and diagonal weights; their weights are
   zeroed before ranking, as the listing does.  Ties rank the lower column
   first.  Sums and the comparison are float64: the total accumulates in
