@@ -14,6 +14,7 @@ import torch
 import block_sparse_attention_amd as bsa
 from block_sparse_attention_amd import inputs as gen
 from oracle import attention as oa
+from oracle import mask as om
 from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
 
 pytestmark = pytest.mark.gpu
@@ -120,3 +121,44 @@ def test_decode_reads_only_selected_blocks(cfg, form):
                 mi = gen.decode_mask_inputs(cfg, 5, base=inp)
                 out = bsa.bsattn_decode_gqa_mask(q, k, v, cu, to_gpu(mi["block_mask"]), num_splits=ns)
         check_close(gpu_bf16_to_f64(out), want, f"poisoned decode {cfg.name} {form} ns{ns}")
+
+
+@pytest.mark.parametrize("kind", ["topk", "threshold"])
+@pytest.mark.parametrize("S,D,causal,dense", [(4096 + 37, 64, True, False), (2048, 128, False, False),
+                                               (9000, 128, True, True)])
+def test_fused_reads_only_selected_blocks(kind, S, D, causal, dense):
+    """The one-launch forms select each row from the block scores in the
+    kernel.  Without the forced diagonal, key blocks whose scores are far
+    below every other score (and below the threshold) are never selected, so
+    their K/V rows can hold NaN; S = 9000 also takes the long-row split."""
+    B, H = 1, 2
+    rng = np.random.default_rng(S + D + int(causal) + (kind == "topk"))
+    nb = -(-S // 64)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D), dtype=np.float32))
+    scores = rng.standard_normal((B, H, nb, nb), dtype=np.float32)
+    kp, vp = k.copy(), v.copy()
+    for h in range(H):
+        cut = rng.choice(np.arange(1, nb), size=3 if dense else max(1, nb // 10), replace=False)
+        scores[0, h, :, cut] = -1e30
+        for j in cut:
+            kp[0, h, 64 * j:64 * j + 64] = NAN_BITS
+            vp[0, h, 64 * j:64 * j + 64] = NAN_BITS
+    # fewer than the uncut columns; N(0, 1) scores above the threshold.  Dense:
+    # rows past 128 blocks, which split
+    topk, thr = (nb - 3, -4.0) if dense else (nb // 2, 0.0)
+    if kind == "topk":
+        m = om.build_mask_topk(scores, topk, False, False)
+    else:
+        m = om.build_mask_threshold(scores, thr, False, False)
+    say(f"[poison-fused] {kind} S={S} D={D} causal={causal} blocks={int(m.sum())}")
+    args = (to_gpu_bf16(q), to_gpu_bf16(kp), to_gpu_bf16(vp), to_gpu(scores))
+    if kind == "topk":
+        got, gm = bsa.bsattn_fwd_topk(*args, topk, False, False, causal, write_mask=True)
+    else:
+        got, gm = bsa.bsattn_fwd_threshold(*args, thr, False, False, causal, write_mask=True)
+    assert np.array_equal(gm.cpu().numpy(), m)
+    f = gen.bf16_bits_to_f64
+    want = oa.prefill(f(q), f(k), f(v), m, causal)
+    check_close(gpu_bf16_to_f64(got), want, f"poisoned fused {kind} S{S} D{D} c{causal}")
