@@ -1,0 +1,129 @@
+"""GPU: tensors past 4 GiB, so every address above 2^32 bytes must be formed
+in 64 bits.  Only the selected blocks hold data; every other K/V row is NaN on
+the device (a read of one would make the output non-finite), and the host
+side keeps just the selected rows.  The expected values come from the oracle
+on the selected blocks laid end to end, which leaves every row's visible keys
+and their causal positions unchanged (the reasoning is given per test).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_amd as bsa
+from block_sparse_attention_amd import inputs as gen
+from oracle import attention as oa
+from tests.gpu_util import check_close, gpu_bf16_to_f64, say, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+GIB = 1 << 30
+
+
+def test_chunk_forward_heads_past_4gib():
+    """One 64-query chunk at the end of the longest key range at D 128, eight
+    heads: K and V are 6.3 GB each, so heads 6 and 7 start past 4 GiB.  The
+    last two key blocks are always selected, so laying the selected blocks
+    end to end keeps the causal relation of every row (as in the chunk
+    tests' longest-range case)."""
+    D, H = 128, 8
+    nbk = bsa.bsattn_fwd_max_key_blocks(D)
+    Sk, Sq = nbk * 64 - 5, 64
+    assert H * Sk * D * 2 > 4 * GIB
+    rng = np.random.default_rng(4242)
+    sel = [sorted(set(rng.integers(0, nbk - 2, 12).tolist()) | {0, nbk - 2, nbk - 1}) for _ in range(H)]
+    q = gen.f32_to_bf16_bits(rng.standard_normal((1, H, Sq, D), dtype=np.float32))
+    nan = float("nan")
+    k_dev = torch.full((1, H, Sk, D), nan, dtype=torch.bfloat16, device="cuda")
+    v_dev = torch.full((1, H, Sk, D), nan, dtype=torch.bfloat16, device="cuda")
+    m = np.zeros((1, H, 1, nbk), np.uint8)
+    kc, vc = [], []
+    for h in range(H):
+        m[0, h, 0, sel[h]] = 1
+        n_rows = sum(min(64, Sk - 64 * j) for j in sel[h])
+        kh = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, D), dtype=np.float32))
+        vh = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, D), dtype=np.float32))
+        pos = 0
+        for j in sel[h]:
+            n = min(64, Sk - 64 * j)
+            k_dev[0, h, 64 * j:64 * j + n] = to_gpu_bf16(kh[pos:pos + n])
+            v_dev[0, h, 64 * j:64 * j + n] = to_gpu_bf16(vh[pos:pos + n])
+            pos += n
+        kc.append(kh)
+        vc.append(vh)
+    say(f"[large-offsets] chunk forward H={H} Sk={Sk} D={D}: K/V {k_dev.numel() * 2 / GIB:.2f} GiB each")
+    got = gpu_bf16_to_f64(bsa.bsattn_fwd_chunk(to_gpu_bf16(q), k_dev, v_dev, to_gpu(m), True))
+    del k_dev, v_dev
+    torch.cuda.empty_cache()
+    f = gen.bf16_bits_to_f64
+    for h in range(H):
+        want = oa.prefill_head_rows(f(q[0, h]), f(kc[h]), f(vc[h]), np.ones((1, len(sel[h])), np.uint8), True)
+        check_close(got[0, h], want, f"chunk forward past 4 GiB h{h}")
+
+
+@pytest.mark.parametrize("form", ["index", "mask"])
+def test_decode_sequences_past_4gib(form):
+    """Three sequences of about two million tokens, eight KV heads, D 128:
+    packed K and V are 12.3 GB each, so the last sequence starts past 8 GiB.
+    The expected values come from the oracle on a packed problem that keeps,
+    per sequence, only the blocks some KV head selects, in order, with the
+    sequence's last (partial) block still last: each query head then sees the
+    same tokens."""
+    B, Hq, Hkv, D = 3, 32, 8, 128
+    lens = np.array([2_000_003, 2_000_064, 1_999_937])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    assert T * Hkv * D * 2 > 8 * GIB
+    rng = np.random.default_rng(777)
+    ms = 24
+    idx = np.full((B, Hkv, ms), -1, np.int32)
+    for b in range(B):
+        nbb = -(-int(lens[b]) // 64)
+        for h in range(Hkv):
+            s = sorted(set(rng.integers(0, nbb - 1, 20).tolist()) | {nbb - 1})[::-1]
+            idx[b, h, :len(s)] = s
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    nan = float("nan")
+    k_dev = torch.full((T, Hkv, D), nan, dtype=torch.bfloat16, device="cuda")
+    v_dev = torch.full((T, Hkv, D), nan, dtype=torch.bfloat16, device="cuda")
+    # the compact problem: per sequence, the union of the selected blocks
+    k_parts, v_parts, cu_c, idx_c = [], [], [0], np.full((B, Hkv, ms), -1, np.int32)
+    for b in range(B):
+        L = int(lens[b])
+        union = sorted({int(j) for j in idx[b].ravel() if j >= 0})
+        n_rows = sum(min(64, L - 64 * j) for j in union)
+        kb = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, Hkv, D), dtype=np.float32))
+        vb = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, Hkv, D), dtype=np.float32))
+        pos, where = 0, {}
+        for p, j in enumerate(union):
+            n = min(64, L - 64 * j)
+            where[j] = p
+            for h in range(Hkv):
+                if j in idx[b, h]:
+                    r0 = int(cu[b]) + 64 * j
+                    k_dev[r0:r0 + n, h] = to_gpu_bf16(kb[pos:pos + n, h])
+                    v_dev[r0:r0 + n, h] = to_gpu_bf16(vb[pos:pos + n, h])
+            pos += n
+        k_parts.append(kb)
+        v_parts.append(vb)
+        cu_c.append(cu_c[-1] + n_rows)
+        for h in range(Hkv):
+            row = [where[int(j)] for j in idx[b, h] if j >= 0]
+            idx_c[b, h, :len(row)] = row
+    cu_c = np.array(cu_c, np.int32)
+    f = gen.bf16_bits_to_f64
+    want = oa.decode_gqa(f(q), f(np.concatenate(k_parts)), f(np.concatenate(v_parts)), cu_c, idx_c)
+    say(f"[large-offsets] decode {form} total_k={T}: K/V {k_dev.numel() * 2 / GIB:.2f} GiB each")
+    qd, cud = to_gpu_bf16(q), to_gpu(cu)
+    for ns in (1, 4):
+        if form == "index":
+            out = bsa.bsattn_decode_gqa(qd, k_dev, v_dev, cud, to_gpu(idx), num_splits=ns)
+        else:
+            nbk = max(-(-int(x) // 64) for x in lens)
+            bm = np.zeros((B, Hkv, nbk), np.uint8)
+            for b in range(B):
+                for h in range(Hkv):
+                    bm[b, h, idx[b, h][idx[b, h] >= 0]] = 1
+            out = bsa.bsattn_decode_gqa_mask(qd, k_dev, v_dev, cud, to_gpu(bm), num_splits=ns)
+        check_close(gpu_bf16_to_f64(out), want, f"decode {form} past 4 GiB ns{ns}")
+    del k_dev, v_dev
+    torch.cuda.empty_cache()
