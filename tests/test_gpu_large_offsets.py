@@ -127,3 +127,70 @@ def test_decode_sequences_past_4gib(form):
         check_close(gpu_bf16_to_f64(out), want, f"decode {form} past 4 GiB ns{ns}")
     del k_dev, v_dev
     torch.cuda.empty_cache()
+
+
+def test_square_forward_heads_past_4gib():
+    """bsattn_fwd on B1 H80 S262144 D128: q, k, v and out are 5 GiB each and
+    the last heads start past 4 GiB (the long-row split's workspace would
+    pass 2 GiB, so rows run whole).  A few work items of heads 0, 40 and 79
+    select scattered blocks and are checked against the oracle; every other
+    item selects key block 0 only with q = 0, so its rows are the mean of
+    block 0's values (a closed form).  K/V rows no item selects are NaN."""
+    B, H, S, D = 1, 80, 262144, 128
+    nb = S // 64
+    assert H * S * D * 2 > 4 * GIB
+    rng = np.random.default_rng(99)
+    heads, qblocks = (0, 40, 79), (1, 2, 2047, nb - 2, nb - 1)
+    m = np.zeros((B, H, nb, nb), np.uint8)
+    m[0, :, :, 0] = 1
+    sel = {}
+    for h in heads:
+        for i in qblocks:
+            s = sorted(set(rng.integers(0, i + 1, 8).tolist()) | {0, i})
+            m[0, h, i, :] = 0
+            m[0, h, i, s] = 1
+            sel[h, i] = s
+    nan = float("nan")
+    q_dev = torch.zeros((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    k_dev = torch.full((B, H, S, D), nan, dtype=torch.bfloat16, device="cuda")
+    v_dev = torch.full((B, H, S, D), nan, dtype=torch.bfloat16, device="cuda")
+    k0 = gen.f32_to_bf16_bits(rng.standard_normal((H, 64, D), dtype=np.float32))
+    v0 = gen.f32_to_bf16_bits(rng.standard_normal((H, 64, D), dtype=np.float32))
+    k_dev[0, :, :64] = to_gpu_bf16(k0)
+    v_dev[0, :, :64] = to_gpu_bf16(v0)
+    host = {}
+    for h in heads:   # host copies: zeros where the device holds NaN (never weighted)
+        qh = np.zeros((S, D), np.uint16)
+        kh = np.zeros((S, D), np.uint16)
+        vh = np.zeros((S, D), np.uint16)
+        kh[:64], vh[:64] = k0[h], v0[h]
+        blocks = sorted({j for i in qblocks for j in sel[h, i]} - {0})
+        for j in blocks:
+            kh[64 * j:64 * j + 64] = gen.f32_to_bf16_bits(rng.standard_normal((64, D), dtype=np.float32))
+            vh[64 * j:64 * j + 64] = gen.f32_to_bf16_bits(rng.standard_normal((64, D), dtype=np.float32))
+            k_dev[0, h, 64 * j:64 * j + 64] = to_gpu_bf16(kh[64 * j:64 * j + 64])
+            v_dev[0, h, 64 * j:64 * j + 64] = to_gpu_bf16(vh[64 * j:64 * j + 64])
+        for i in qblocks:
+            qh[64 * i:64 * i + 64] = gen.f32_to_bf16_bits(rng.standard_normal((64, D), dtype=np.float32))
+            q_dev[0, h, 64 * i:64 * i + 64] = to_gpu_bf16(qh[64 * i:64 * i + 64])
+        host[h] = (qh, kh, vh)
+    assert bsa.bsattn_fwd_workspace_bytes(B, H, S, D) == 0
+    say(f"[large-offsets] square forward B{B} H{H} S{S} D{D}: q/k/v/out {q_dev.numel() * 2 / GIB:.2f} GiB each")
+    out = bsa.bsattn_fwd(q_dev, k_dev, v_dev, to_gpu(m), True)
+    f = gen.bf16_bits_to_f64
+    for h in heads:
+        qh, kh, vh = host[h]
+        rows = np.array([64 * i + r for i in qblocks for r in (0, 31, 63)])
+        got = gpu_bf16_to_f64(out[0, h, torch.from_numpy(rows).cuda()])
+        want = oa.prefill_head_rows(f(qh), f(kh), f(vh), m[0, h], True, rows)
+        check_close(got, want, f"square forward past 4 GiB h{h}")
+    # items that see block 0 only, with q = 0: every visible key weighs the same
+    for h in (1, 41, 78, 79):
+        for i in (5, 3000, nb - 1):
+            if (h, i) in sel:
+                continue
+            got = gpu_bf16_to_f64(out[0, h, 64 * i:64 * i + 64])
+            want = np.broadcast_to(f(v0[h]).mean(axis=0), got.shape)
+            check_close(got, want, f"square forward past 4 GiB, block 0 only, h{h} i{i}")
+    del q_dev, k_dev, v_dev, out
+    torch.cuda.empty_cache()
