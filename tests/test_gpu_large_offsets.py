@@ -194,3 +194,68 @@ def test_square_forward_heads_past_4gib():
             check_close(got, want, f"square forward past 4 GiB, block 0 only, h{h} i{i}")
     del q_dev, k_dev, v_dev, out
     torch.cuda.empty_cache()
+
+
+def test_paged_decode_cache_past_4gib():
+    """Paged decode over a 10 000-page cache (256-token pages, eight KV
+    heads, D 128: K and V caches of 4.9 GiB each), pages handed out in a
+    shuffled order so blocks sit anywhere in the cache.  Expected values: the
+    oracle's packed decode on the union of the selected blocks, laid end to
+    end per sequence with the last (partial) block still last, as in the
+    packed test above."""
+    B, Hq, Hkv, D, ps = 2, 32, 8, 128, 256
+    lens = np.array([1_000_037, 999_999])
+    per_seq = [-(-int(x) // ps) for x in lens]
+    num_pages = 10_000
+    assert num_pages * ps * Hkv * D * 2 > 4 * GIB and sum(per_seq) < num_pages
+    rng = np.random.default_rng(31337)
+    perm = rng.permutation(num_pages)
+    table = np.full((B, max(per_seq)), -1, np.int32)
+    p = 0
+    for b in range(B):
+        table[b, :per_seq[b]] = perm[p:p + per_seq[b]]
+        p += per_seq[b]
+    ms = 24
+    idx = np.full((B, Hkv, ms), -1, np.int32)
+    for b in range(B):
+        nbb = -(-int(lens[b]) // 64)
+        for h in range(Hkv):
+            s = sorted(set(rng.integers(0, nbb - 1, 20).tolist()) | {nbb - 1})[::-1]
+            idx[b, h, :len(s)] = s
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    nan = float("nan")
+    kc = torch.full((num_pages, ps, Hkv, D), nan, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((num_pages, ps, Hkv, D), nan, dtype=torch.bfloat16, device="cuda")
+    k_parts, v_parts, cu_c, idx_c = [], [], [0], np.full((B, Hkv, ms), -1, np.int32)
+    for b in range(B):
+        L = int(lens[b])
+        union = sorted({int(j) for j in idx[b].ravel() if j >= 0})
+        n_rows = sum(min(64, L - 64 * j) for j in union)
+        kb = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, Hkv, D), dtype=np.float32))
+        vb = gen.f32_to_bf16_bits(rng.standard_normal((n_rows, Hkv, D), dtype=np.float32))
+        pos, where = 0, {}
+        for pidx, j in enumerate(union):
+            n = min(64, L - 64 * j)
+            where[j] = pidx
+            page, r0 = int(table[b, (64 * j) // ps]), (64 * j) % ps
+            for h in range(Hkv):
+                if j in idx[b, h]:
+                    kc[page, r0:r0 + n, h] = to_gpu_bf16(kb[pos:pos + n, h])
+                    vc[page, r0:r0 + n, h] = to_gpu_bf16(vb[pos:pos + n, h])
+            pos += n
+        k_parts.append(kb)
+        v_parts.append(vb)
+        cu_c.append(cu_c[-1] + n_rows)
+        for h in range(Hkv):
+            row = [where[int(j)] for j in idx[b, h] if j >= 0]
+            idx_c[b, h, :len(row)] = row
+    f = gen.bf16_bits_to_f64
+    want = oa.decode_gqa(f(q), f(np.concatenate(k_parts)), f(np.concatenate(v_parts)),
+                         np.array(cu_c, np.int32), idx_c)
+    say(f"[large-offsets] paged decode {num_pages} pages: caches {kc.numel() * 2 / GIB:.2f} GiB each")
+    for ns in (1, 4):
+        out = bsa.bsattn_decode_gqa_paged(to_gpu_bf16(q), kc, vc, to_gpu(lens.astype(np.int32)),
+                                          to_gpu(table), to_gpu(idx), num_splits=ns)
+        check_close(gpu_bf16_to_f64(out), want, f"paged decode past 4 GiB ns{ns}")
+    del kc, vc
+    torch.cuda.empty_cache()
