@@ -259,3 +259,45 @@ def test_paged_decode_cache_past_4gib():
         check_close(gpu_bf16_to_f64(out), want, f"paged decode past 4 GiB ns{ns}")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+def test_xattn_estimate_heads_past_4gib():
+    """The whole estimate at stride 8 on B1 H270 S65536 D128 (the longest key
+    range the block sums and the selection take): q and k are 4.2 GiB each
+    and the log-sum workspace 8.4 GiB, so the last heads' operands and
+    log-sums sit past 4 GiB.  Heads 0 and 269 hold seeded N(0, 1) data and
+    head 268 zeros (a uniform softmax); all three are checked against the
+    oracle, and their selections are checked valid for the oracle's sums."""
+    from tests.gpu_util import parallel_map
+    from tests.test_gpu_xattn import SUM_ATOL, SUM_RTOL, _check_valid_selection
+    from oracle import xattn as ox
+
+    B, H, S, D, stride = 1, 270, 65536, 128, 8
+    assert H * S * D * 2 > 4 * GIB
+    rng = np.random.default_rng(2718)
+    q_dev = torch.zeros((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    k_dev = torch.zeros((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    host = {}
+    for h in (0, 269):
+        qh = gen.f32_to_bf16_bits(rng.standard_normal((S, D), dtype=np.float32))
+        kh = gen.f32_to_bf16_bits(rng.standard_normal((S, D), dtype=np.float32))
+        q_dev[0, h] = to_gpu_bf16(qh)
+        k_dev[0, h] = to_gpu_bf16(kh)
+        host[h] = (qh, kh)
+    host[268] = (np.zeros((S, D), np.uint16), np.zeros((S, D), np.uint16))
+    say(f"[large-offsets] xattn estimate B{B} H{H} S{S} D{D}: q/k {q_dev.numel() * 2 / GIB:.2f} GiB each")
+    mask, sums = bsa.bsattn_xattn_estimate(q_dev, k_dev, stride, 1.0, 0.9, True, True, True,
+                                           write_sums=True)
+    heads = sorted(host)
+    got_s = {h: sums[:, h:h + 1].cpu().numpy() for h in heads}
+    got_m = {h: mask[:, h:h + 1].cpu().numpy() for h in heads}
+    del q_dev, k_dev, mask, sums
+    torch.cuda.empty_cache()
+    f = gen.bf16_bits_to_f64
+    wants = parallel_map(lambda h: ox.block_sums(f(host[h][0])[None, None], f(host[h][1])[None, None],
+                                                 stride, 1.0, True), heads, workers=3)
+    tol = 1024 * (SUM_ATOL + SUM_RTOL * 8)
+    for h, want in zip(heads, wants):
+        np.testing.assert_allclose(got_s[h], want, rtol=SUM_RTOL, atol=SUM_ATOL)
+        _check_valid_selection(got_m[h], want, 0.9, True, True, True, tol)
+        say(f"  head {h}: block sums and selection ok")
